@@ -1,0 +1,252 @@
+"""Python binding of libskiparse (Skiparse-2D sparse attention forward on
+MI355X).  Argument marshalling only: every step of the computation runs in the
+library's HIP kernels.  PyTorch supplies device memory and the current stream.
+
+The names mirror the C ABI in include/skiparse.h:
+
+    skiparse_abi_version()
+    skiparse_plan_init(B, T, H, W, heads, d, k, mode) -> SkiparsePlan
+    skiparse_plan_index_map(plan) -> numpy int32 (n_sub, sub_len_padded)
+    skiparse_index_map_device(plan, out, stream=None)
+    skiparse_attn_fwd(plan, dtype, q, k, v, o, softmax_scale=0.0,
+                      descale_qkv=None, sub_begin=0, sub_count=0, stream=None)
+    skiparse_quant_fp8_workspace_bytes(numel)
+    skiparse_quant_fp8(x, y, scale, fp8_max=448.0, eps=1e-12,
+                       workspace=None, stream=None)
+    skiparse_last_error()
+
+plus two conveniences that allocate their outputs with torch:
+``attention(q, k, v, kf, mode)`` and ``quantize_fp8(x)``.
+
+There is no fallback: if libskiparse.so is missing the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libskiparse.so")
+
+OK = 0
+EINVAL = -1
+EUNSUPPORTED = -2
+EHIP = -3
+EWORKSPACE = -4
+
+MODE_TOKEN = 0
+MODE_GROUP = 1
+
+F32 = 0
+BF16 = 1
+FP8_E4M3 = 2
+
+MAX_K = 8
+ABI_VERSION = 1
+
+EXPORTED = (
+    "skiparse_abi_version",
+    "skiparse_plan_init",
+    "skiparse_plan_index_map",
+    "skiparse_index_map_device",
+    "skiparse_attn_fwd",
+    "skiparse_quant_fp8_workspace_bytes",
+    "skiparse_quant_fp8",
+    "skiparse_last_error",
+)
+
+
+class SkiparsePlan(ctypes.Structure):
+    """Mirror of ``skiparse_plan`` (plain data)."""
+    _fields_ = [
+        ("abi", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("d", ctypes.c_int32), ("k", ctypes.c_int32), ("mode", ctypes.c_int32),
+        ("Hp", ctypes.c_int32), ("Wp", ctypes.c_int32),
+        ("sub_h", ctypes.c_int32), ("sub_w", ctypes.c_int32),
+        ("n_sub", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("sub_len_padded", ctypes.c_int64),
+        ("pairs", ctypes.c_int64),
+        ("real_h", ctypes.c_int32 * MAX_K),
+        ("real_w", ctypes.c_int32 * MAX_K),
+    ]
+
+    @property
+    def flops(self) -> int:
+        """Algorithmic FLOPs of one call over all subsequences: 4 * d * pairs."""
+        return 4 * self.d * self.pairs
+
+    def sub_lengths(self):
+        k = self.k
+        return [self.T * self.real_h[p] * self.real_w[q] for p in range(k) for q in range(k)]
+
+
+class SkiparseError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"skiparse error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libskiparse.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m fixed_pattern_sparse_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(SkiparsePlan)
+    vp = ctypes.c_void_p
+    L.skiparse_abi_version.restype = ctypes.c_int
+    L.skiparse_abi_version.argtypes = []
+    L.skiparse_plan_init.restype = ctypes.c_int
+    L.skiparse_plan_init.argtypes = [P] + [ctypes.c_int32] * 8
+    L.skiparse_plan_index_map.restype = ctypes.c_int
+    L.skiparse_plan_index_map.argtypes = [P, vp]
+    L.skiparse_index_map_device.restype = ctypes.c_int
+    L.skiparse_index_map_device.argtypes = [P, vp, vp]
+    L.skiparse_attn_fwd.restype = ctypes.c_int
+    L.skiparse_attn_fwd.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, ctypes.c_float, vp,
+                                    ctypes.c_int32, ctypes.c_int32, vp]
+    L.skiparse_quant_fp8_workspace_bytes.restype = ctypes.c_size_t
+    L.skiparse_quant_fp8_workspace_bytes.argtypes = [ctypes.c_int64]
+    L.skiparse_quant_fp8.restype = ctypes.c_int
+    L.skiparse_quant_fp8.argtypes = [vp, ctypes.c_int, ctypes.c_int64, vp, vp, ctypes.c_float, ctypes.c_float,
+                                     vp, ctypes.c_size_t, vp]
+    L.skiparse_last_error.restype = ctypes.c_char_p
+    L.skiparse_last_error.argtypes = []
+    if L.skiparse_abi_version() != ABI_VERSION:
+        raise RuntimeError("libskiparse ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _check(code):
+    if code != OK:
+        raise SkiparseError(code, skiparse_last_error())
+
+
+def _ptr(x):
+    """Device/host address of a torch tensor, or an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def skiparse_abi_version() -> int:
+    return lib().skiparse_abi_version()
+
+
+def skiparse_last_error() -> str:
+    return lib().skiparse_last_error().decode()
+
+
+def skiparse_plan_init(B, T, H, W, heads, d, k, mode) -> SkiparsePlan:
+    plan = SkiparsePlan()
+    _check(lib().skiparse_plan_init(ctypes.byref(plan), B, T, H, W, heads, d, k, mode))
+    return plan
+
+
+def skiparse_plan_index_map(plan: SkiparsePlan) -> np.ndarray:
+    out = np.empty((plan.n_sub, plan.sub_len_padded), np.int32)
+    _check(lib().skiparse_plan_index_map(ctypes.byref(plan), out.ctypes.data))
+    return out
+
+
+def skiparse_index_map_device(plan: SkiparsePlan, out, stream=None):
+    """Write the device index map into ``out`` (int32 device tensor with
+    n_sub * sub_len_padded elements)."""
+    if out.numel() != plan.n_sub * plan.sub_len_padded:
+        raise ValueError("out has the wrong number of elements")
+    _check(lib().skiparse_index_map_device(ctypes.byref(plan), _ptr(out), _stream(stream)))
+    return out
+
+
+def skiparse_attn_fwd(plan: SkiparsePlan, dtype: int, q, k, v, o, softmax_scale: float = 0.0,
+                      descale_qkv=None, sub_begin: int = 0, sub_count: int = 0, stream=None):
+    _check(lib().skiparse_attn_fwd(ctypes.byref(plan), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   float(softmax_scale), _ptr(descale_qkv), sub_begin, sub_count,
+                                   _stream(stream)))
+    return o
+
+
+def skiparse_quant_fp8_workspace_bytes(numel: int) -> int:
+    return int(lib().skiparse_quant_fp8_workspace_bytes(numel))
+
+
+def skiparse_quant_fp8(x, y, scale, fp8_max: float = 448.0, eps: float = 1e-12, workspace=None,
+                       stream=None, x_dtype=None):
+    """Quantize the whole tensor ``x`` (bf16 or fp32, device) into ``y`` (uint8,
+    same numel); ``scale`` receives {scale, 1/scale} (2 fp32, device)."""
+    import torch
+    if x_dtype is None:
+        x_dtype = BF16 if x.dtype == torch.bfloat16 else F32
+    numel = x.numel()
+    if workspace is None:
+        nb = skiparse_quant_fp8_workspace_bytes(numel)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    wb = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    _check(lib().skiparse_quant_fp8(_ptr(x), x_dtype, numel, _ptr(y), _ptr(scale), float(fp8_max), float(eps),
+                                    _ptr(workspace), wb, _stream(stream)))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# conveniences (torch allocates, the library computes)
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.uint8 or t.dtype == getattr(torch, "float8_e4m3fn", None):
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def attention(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, descale_qkv=None, out=None,
+              sub_begin: int = 0, sub_count: int = 0, plan: SkiparsePlan | None = None):
+    """Skiparse-2D attention forward on (B, T, H, W, heads, d) device tensors."""
+    import torch
+    if q.dim() != 6 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one (B, T, H, W, heads, d) shape")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    B, T, H, W, nh, d = q.shape
+    code = _dtype_code(q)
+    if plan is None:
+        plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
+    if out is None:
+        odt = torch.float32 if code == F32 else torch.bfloat16
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
+    skiparse_attn_fwd(plan, code, q, k, v, out, softmax_scale, descale_qkv, sub_begin, sub_count)
+    return out
+
+
+def quantize_fp8(x, fp8_max: float = 448.0, eps: float = 1e-12):
+    """Per-tensor e4m3 quantization: returns (codes uint8, scale pair fp32[2])."""
+    import torch
+    y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    sc = torch.empty(2, dtype=torch.float32, device=x.device)
+    skiparse_quant_fp8(x.contiguous(), y, sc, fp8_max, eps)
+    return y, sc

@@ -1,0 +1,275 @@
+// C ABI of libskiparse: argument validation, the host plan, and dispatch to
+// the HIP kernels.  See include/skiparse.h for the contract of each call.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+using namespace skiparse;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return SKIPARSE_OK;
+}
+
+// Real local extent on one axis for coordinate p (any-resolution rule: the
+// real members are a prefix of the local axis).
+int32_t real_extent(int32_t n, int32_t k, int32_t mode, int32_t p) {
+  if (k == 1) return n;
+  if (mode == SKIPARSE_MODE_TOKEN) return n / k + (p < n % k ? 1 : 0);
+  const int32_t kk = k * k;
+  int32_t r = n % kk - p * k;
+  r = r < 0 ? 0 : (r > k ? k : r);
+  return (n / kk) * k + r;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Re-derive a plan from its inputs and compare, so a hand-edited or stale
+// struct is refused instead of driving the kernels out of bounds.
+int check_plan(const skiparse_plan* p) {
+  if (!p) return fail(SKIPARSE_EINVAL, "plan is NULL");
+  if (p->abi != SKIPARSE_ABI_VERSION) return fail(SKIPARSE_EINVAL, "plan has ABI %d, library %d", p->abi, SKIPARSE_ABI_VERSION);
+  skiparse_plan q;
+  const std::string saved = g_err;
+  if (skiparse_plan_init(&q, p->B, p->T, p->H, p->W, p->heads, p->d, p->k, p->mode) != SKIPARSE_OK)
+    return fail(SKIPARSE_EINVAL, "plan fields are invalid: %s", g_err.c_str());
+  if (std::memcmp(&q, p, sizeof q) != 0) return fail(SKIPARSE_EINVAL, "plan was modified after skiparse_plan_init");
+  g_err = saved;
+  return SKIPARSE_OK;
+}
+
+void make_geom(const skiparse_plan& p, Geom& g) {
+  g.T = p.T;
+  g.H = p.H;
+  g.W = p.W;
+  g.k = p.k;
+  g.mode = p.mode;
+  g.div_k = make_fastdiv((uint32_t)p.k);
+}
+
+SubGeom make_sub(const skiparse_plan& p, int s) {
+  SubGeom sg;
+  const int pp = s / p.k, qq = s % p.k;
+  const int32_t hr = p.real_h[pp], wr = p.real_w[qq];
+  sg.n = p.T * hr * wr;
+  sg.p = pp;
+  sg.q = qq;
+  sg.tile0 = 0;
+  sg.div_hw = make_fastdiv((uint32_t)(hr * wr > 0 ? hr * wr : 1));
+  sg.div_w = make_fastdiv((uint32_t)(wr > 0 ? wr : 1));
+  if (hr * wr == 0) {   // keep the stored extents exact for the map writer
+    sg.div_hw.d = (uint32_t)(hr * wr);
+    sg.div_w.d = (uint32_t)wr;
+    sg.n = 0;
+  }
+  return sg;
+}
+
+}  // namespace
+
+extern "C" {
+
+int skiparse_abi_version(void) { return SKIPARSE_ABI_VERSION; }
+
+const char* skiparse_last_error(void) { return g_err.c_str(); }
+
+int skiparse_plan_init(skiparse_plan* plan, int32_t B, int32_t T, int32_t H, int32_t W, int32_t heads,
+                       int32_t d, int32_t k, int32_t mode) {
+  if (!plan) return fail(SKIPARSE_EINVAL, "plan is NULL");
+  if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || d < 1)
+    return fail(SKIPARSE_EINVAL, "every extent must be >= 1 (B=%d T=%d H=%d W=%d heads=%d d=%d)", B, T, H, W, heads, d);
+  if (k < 1 || k > SKIPARSE_MAX_K) return fail(SKIPARSE_EINVAL, "k=%d outside [1, %d]", k, SKIPARSE_MAX_K);
+  if (mode != SKIPARSE_MODE_TOKEN && mode != SKIPARSE_MODE_GROUP) return fail(SKIPARSE_EINVAL, "mode=%d is not token (0) or group (1)", mode);
+  const int64_t kk = (int64_t)k * k;
+  const int64_t Hp = (H + kk - 1) / kk * kk, Wp = (W + kk - 1) / kk * kk;
+  const int64_t tokens = (int64_t)T * H * W;
+  const int64_t padded = (int64_t)T * Hp * Wp;
+  if (padded >= (int64_t(1) << 31)) return fail(SKIPARSE_EINVAL, "T*Hp*Wp = %lld must stay below 2^31", (long long)padded);
+  const double numel = (double)B * tokens * heads * d;
+  if (numel >= 4.6e18 || (int64_t)heads * d >= (int64_t(1) << 31))
+    return fail(SKIPARSE_EINVAL, "tensor too large");
+  std::memset(plan, 0, sizeof *plan);
+  plan->abi = SKIPARSE_ABI_VERSION;
+  plan->B = B;
+  plan->T = T;
+  plan->H = H;
+  plan->W = W;
+  plan->heads = heads;
+  plan->d = d;
+  plan->k = k;
+  plan->mode = k == 1 ? SKIPARSE_MODE_TOKEN : mode;
+  plan->Hp = (int32_t)Hp;
+  plan->Wp = (int32_t)Wp;
+  plan->sub_h = (int32_t)(Hp / k);
+  plan->sub_w = (int32_t)(Wp / k);
+  plan->n_sub = (int32_t)kk;
+  plan->sub_len_padded = (int64_t)T * plan->sub_h * plan->sub_w;
+  for (int p = 0; p < k; ++p) {
+    plan->real_h[p] = real_extent(H, k, plan->mode, p);
+    plan->real_w[p] = real_extent(W, k, plan->mode, p);
+  }
+  double pairs = 0;
+  int64_t pairs_i = 0;
+  for (int p = 0; p < k; ++p)
+    for (int q = 0; q < k; ++q) {
+      const int64_t n = (int64_t)T * plan->real_h[p] * plan->real_w[q];
+      pairs += (double)n * n;
+      pairs_i += n * n;
+    }
+  if (pairs * B * heads >= 9.0e18) return fail(SKIPARSE_EINVAL, "pair count overflows int64");
+  plan->pairs = pairs_i * B * heads;
+  return ok();
+}
+
+int skiparse_plan_index_map(const skiparse_plan* plan, int32_t* host_gather) {
+  if (int e = check_plan(plan)) return e;
+  if (!host_gather) return fail(SKIPARSE_EINVAL, "host_gather is NULL");
+  Geom g;
+  make_geom(*plan, g);
+  const int64_t L = plan->sub_len_padded;
+  for (int s = 0; s < plan->n_sub; ++s) {
+    const SubGeom sg = make_sub(*plan, s);
+    const int32_t hr = plan->real_h[s / plan->k], wr = plan->real_w[s % plan->k];
+    int32_t* row = host_gather + (int64_t)s * L;
+    int64_t x = 0;
+    for (int32_t t = 0; t < plan->T; ++t)
+      for (int32_t hl = 0; hl < plan->sub_h; ++hl)
+        for (int32_t wl = 0; wl < plan->sub_w; ++wl, ++x) {
+          if (hl < hr && wl < wr) {
+            const uint32_t j = ((uint32_t)t * hr + hl) * (uint32_t)wr + wl;
+            row[x] = (int32_t)token_of(j, sg, g);
+          } else {
+            row[x] = -1;
+          }
+        }
+  }
+  return ok();
+}
+
+int skiparse_index_map_device(const skiparse_plan* plan, int32_t* dev_gather, hipStream_t stream) {
+  if (int e = check_plan(plan)) return e;
+  if (!dev_gather) return fail(SKIPARSE_EINVAL, "dev_gather is NULL");
+  if (((uintptr_t)dev_gather & 3u) != 0) return fail(SKIPARSE_EINVAL, "dev_gather must be 4-byte aligned");
+  Geom g;
+  make_geom(*plan, g);
+  SubGeom subs[kMaxRun];
+  for (int s = 0; s < plan->n_sub; ++s) subs[s] = make_sub(*plan, s);
+  (void)hipGetLastError();
+  const hipError_t e = launch_index_map(g, subs, plan->n_sub, plan->sub_h, plan->sub_w, dev_gather, stream);
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "index map launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int skiparse_attn_fwd(const skiparse_plan* plan, skiparse_dtype dtype, const void* q, const void* k, const void* v,
+                      void* o, float softmax_scale, const float* dev_descale_qkv, int32_t sub_begin,
+                      int32_t sub_count, hipStream_t stream) {
+  if (int e = check_plan(plan)) return e;
+  const int d = plan->d;
+  size_t in_elt, out_elt;
+  switch (dtype) {
+    case SKIPARSE_F32: in_elt = 4; out_elt = 4; break;
+    case SKIPARSE_BF16: in_elt = 2; out_elt = 2; break;
+    case SKIPARSE_FP8_E4M3: in_elt = 1; out_elt = 2; break;
+    default: return fail(SKIPARSE_EINVAL, "unknown dtype %d", (int)dtype);
+  }
+  if (dtype == SKIPARSE_FP8_E4M3) {
+    if (d != 128) return fail(SKIPARSE_EUNSUPPORTED, "FP8 attention is built for d=128 only (d=%d)", d);
+    if (!dev_descale_qkv) return fail(SKIPARSE_EINVAL, "FP8 needs dev_descale_qkv");
+    if (((uintptr_t)dev_descale_qkv & 3u) != 0) return fail(SKIPARSE_EINVAL, "dev_descale_qkv must be 4-byte aligned");
+  } else {
+    if (d != 64 && d != 128) return fail(SKIPARSE_EUNSUPPORTED, "d=%d is not built (64 or 128)", d);
+    if (dev_descale_qkv) return fail(SKIPARSE_EINVAL, "dev_descale_qkv must be NULL unless dtype is FP8");
+  }
+  if (!q || !k || !v || !o) return fail(SKIPARSE_EINVAL, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SKIPARSE_EINVAL, "q, k, v and o must be 16-byte aligned");
+  const int64_t numel = (int64_t)plan->B * plan->T * plan->H * plan->W * plan->heads * d;
+  if (overlap(o, numel * out_elt, q, numel * in_elt) || overlap(o, numel * out_elt, k, numel * in_elt) ||
+      overlap(o, numel * out_elt, v, numel * in_elt))
+    return fail(SKIPARSE_EINVAL, "o must not overlap q, k or v");
+  if (sub_count == 0) {
+    if (sub_begin != 0) return fail(SKIPARSE_EINVAL, "sub_count == 0 (all) needs sub_begin == 0");
+    sub_count = plan->n_sub;
+  }
+  if (sub_begin < 0 || sub_count < 0 || sub_begin + sub_count > plan->n_sub)
+    return fail(SKIPARSE_EINVAL, "subsequence range [%d, %d) outside [0, %d)", sub_begin, sub_begin + sub_count, plan->n_sub);
+  if (!(std::isfinite(softmax_scale))) return fail(SKIPARSE_EINVAL, "softmax_scale must be finite");
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
+
+  AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.descale = dev_descale_qkv;
+  a.batch_stride = (int64_t)plan->T * plan->H * plan->W * plan->heads * d;
+  a.row_stride = plan->heads * d;
+  a.heads = plan->heads;
+  a.n_run = sub_count;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  make_geom(*plan, a.g);
+  for (int i = 0; i < sub_count; ++i) a.sub[i] = make_sub(*plan, sub_begin + i);
+
+  (void)hipGetLastError();   // drop an error left by unrelated earlier work
+  hipError_t e;
+  switch (dtype) {
+    case SKIPARSE_F32: e = launch_attn_f32(a, plan->B, d, stream); break;
+    case SKIPARSE_BF16: e = launch_attn_bf16(a, plan->B, d, stream); break;
+    default: e = launch_attn_fp8(a, plan->B, d, stream); break;
+  }
+  if (e == hipErrorNotSupported) return fail(SKIPARSE_EUNSUPPORTED, "this dtype has no kernel in this build");
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t skiparse_quant_fp8_workspace_bytes(int64_t numel) { return quant_workspace_bytes(numel < 0 ? 0 : numel); }
+
+int skiparse_quant_fp8(const void* x, skiparse_dtype x_dtype, int64_t numel, uint8_t* y, float* dev_scale,
+                       float fp8_max, float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (x_dtype != SKIPARSE_BF16 && x_dtype != SKIPARSE_F32)
+    return fail(SKIPARSE_EINVAL, "x_dtype must be BF16 or F32");
+  if (numel < 1) return fail(SKIPARSE_EINVAL, "numel must be >= 1");
+  if (!x || !y || !dev_scale) return fail(SKIPARSE_EINVAL, "x, y and dev_scale must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)dev_scale & 3u) != 0)
+    return fail(SKIPARSE_EINVAL, "x and y must be 16-byte aligned, dev_scale 4-byte aligned");
+  if (!(fp8_max > 0.f) || !std::isfinite(fp8_max) || !(eps >= 0.f) || !std::isfinite(eps))
+    return fail(SKIPARSE_EINVAL, "fp8_max must be positive and eps non-negative, both finite");
+  const size_t need = quant_workspace_bytes(numel);
+  if (!workspace || workspace_bytes < need)
+    return fail(SKIPARSE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (((uintptr_t)workspace & 3u) != 0) return fail(SKIPARSE_EINVAL, "workspace must be 4-byte aligned");
+  const size_t xb = (size_t)numel * (x_dtype == SKIPARSE_BF16 ? 2 : 4);
+  if (overlap(y, (size_t)numel, x, xb) || overlap(workspace, need, x, xb) || overlap(workspace, need, y, (size_t)numel))
+    return fail(SKIPARSE_EINVAL, "x, y and workspace must not overlap");
+  (void)hipGetLastError();
+  const hipError_t e = launch_quant_fp8(x, x_dtype == SKIPARSE_BF16, numel, y, dev_scale, fp8_max, eps, workspace, stream);
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "quantization launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Per-tensor 8-bit quantization with the pages' scale rule
+// scale = FP8max / (Amax + eps), Amax = max |x| over the whole tensor, one
+// scale per tensor (OSP-Next summary, 方法步骤详情 method steps).  The pages'
+// HiF8 format is replaced by OCP e4m3 (largest finite value 448).
+//
+// Three streaming passes, all HBM-bound:
+//   1. per-work-group max |x| into the workspace (16-byte loads);
+//   2. one work-group reduces the partial maxima and writes {scale, 1/scale},
+//      each an IEEE fp32 division;
+//   3. y = e4m3(x * scale): the fp32 product is clamped to +-448 and
+//      converted by v_cvt_pk_fp8_f32 (round to nearest even), which equals
+//      round-to-nearest-even with saturation.
+#include "internal.h"
+
+namespace skiparse {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxBlocks = 2048;
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float block_max(float v) {
+  __shared__ float part[kThreads / 64];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = part[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, part[i]);
+  return r;
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) amax_partial_kernel(const void* __restrict__ x, int64_t numel,
+                                                                 float* __restrict__ part) {
+  float m = 0.f;
+  constexpr int VE = BF16 ? 8 : 4;   // elements per 16-byte vector
+  const int64_t nvec = numel / VE;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+    const uint4 u = ((const uint4*)x)[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if (BF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[e] & 0xFFFFu)));
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[e] >> 16)));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(__uint_as_float(w[e])));
+    }
+  }
+  if (blockIdx.x == 0) {   // scalar tail
+    for (int64_t i = nvec * VE + threadIdx.x; i < numel; i += kThreads) {
+      const float v = BF16 ? bf16_bits_to_f32(((const uint16_t*)x)[i]) : ((const float*)x)[i];
+      m = fmaxf(m, fabsf(v));
+    }
+  }
+  m = block_max(m);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+__global__ void __launch_bounds__(kThreads) scale_kernel(const float* __restrict__ part, int nparts, float fp8_max,
+                                                         float eps, float* __restrict__ scale) {
+  float m = 0.f;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) m = fmaxf(m, part[i]);
+  m = block_max(m);
+  if (threadIdx.x == 0) {
+    const float s = fp8_max / (m + eps);
+    scale[0] = s;
+    scale[1] = 1.0f / s;
+  }
+}
+
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d, float s) {
+  auto sat = [](float v) { return fminf(fmaxf(v, -kE4M3Max), kE4M3Max); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a * s), sat(b * s), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c * s), sat(d * s), w, true);
+  return (uint32_t)w;
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) quantize_kernel(const void* __restrict__ x, int64_t numel,
+                                                            const float* __restrict__ scale, uint8_t* __restrict__ y) {
+  const float s = scale[0];
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  if (BF16) {
+    const int64_t nvec = numel / 8;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+      const uint4 u = ((const uint4*)x)[i];
+      uint2 o;
+      o.x = cvt4(bf16_bits_to_f32(u.x & 0xFFFFu), bf16_bits_to_f32(u.x >> 16), bf16_bits_to_f32(u.y & 0xFFFFu),
+                 bf16_bits_to_f32(u.y >> 16), s);
+      o.y = cvt4(bf16_bits_to_f32(u.z & 0xFFFFu), bf16_bits_to_f32(u.z >> 16), bf16_bits_to_f32(u.w & 0xFFFFu),
+                 bf16_bits_to_f32(u.w >> 16), s);
+      ((uint2*)y)[i] = o;
+    }
+    if (blockIdx.x == 0) {
+      for (int64_t i = nvec * 8 + threadIdx.x; i < numel; i += kThreads) {
+        const float v = bf16_bits_to_f32(((const uint16_t*)x)[i]);
+        y[i] = (uint8_t)(cvt4(v, 0.f, 0.f, 0.f, s) & 0xFF);
+      }
+    }
+  } else {
+    const int64_t nvec = numel / 4;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+      const float4 v = ((const float4*)x)[i];
+      ((uint32_t*)y)[i] = cvt4(v.x, v.y, v.z, v.w, s);
+    }
+    if (blockIdx.x == 0) {
+      for (int64_t i = nvec * 4 + threadIdx.x; i < numel; i += kThreads)
+        y[i] = (uint8_t)(cvt4(((const float*)x)[i], 0.f, 0.f, 0.f, s) & 0xFF);
+    }
+  }
+}
+
+int blocks_for(int64_t numel) {
+  int64_t b = (numel + 16383) / 16384;
+  if (b < 1) b = 1;
+  if (b > kMaxBlocks) b = kMaxBlocks;
+  return (int)b;
+}
+
+}  // namespace
+
+size_t quant_workspace_bytes(int64_t numel) { return (size_t)blocks_for(numel) * sizeof(float); }
+
+hipError_t launch_quant_fp8(const void* x, int x_is_bf16, int64_t numel, uint8_t* y, float* scale,
+                            float fp8_max, float eps, void* ws, hipStream_t stream) {
+  const int nb = blocks_for(numel);
+  float* part = (float*)ws;
+  if (x_is_bf16)
+    hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(nb), dim3(kThreads), 0, stream, x, numel, part);
+  else
+    hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(nb), dim3(kThreads), 0, stream, x, numel, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scale_kernel, dim3(1), dim3(kThreads), 0, stream, part, nb, fp8_max, eps, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int qb = nb;
+  if (x_is_bf16)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3(qb), dim3(kThreads), 0, stream, x, numel, scale, y);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3(qb), dim3(kThreads), 0, stream, x, numel, scale, y);
+  return hipGetLastError();
+}
+
+}  // namespace skiparse

@@ -1,0 +1,179 @@
+/*
+ * skiparse.h -- C ABI of libskiparse, Skiparse-2D sparse attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (OSP-Next summary page, 核心方法 "core method" and
+ * 方法步骤详情 "method steps"; OSP-Next abstract):
+ *   video tokens (B, T, H, W, heads, d) are regrouped by a fixed rule into k*k
+ *   independent subsequences; dense softmax attention runs inside each
+ *   subsequence; every output row is written back at its token's original
+ *   position.
+ *     token-wise  (pixel unshuffle): token (h, w) joins subsequence
+ *                 s = (h mod k) * k + (w mod k);
+ *     group-wise  (patch unshuffle of k x k blocks, block index mod k):
+ *                 s = ((h / k) mod k) * k + ((w / k) mod k).
+ *   When H or W is not a multiple of k*k the grid is padded at the high end
+ *   to the next multiple and the padded tokens are masked (any-resolution
+ *   rule), so that a position follows the same pattern at every resolution.
+ *   k = 1 is plain full attention (the hybrid model's full-attention layers).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device memory owned by the caller; the library
+ *     never allocates, frees or synchronizes.  All device work is enqueued on
+ *     the given stream and runs asynchronously.
+ *   - Tensors are contiguous (B, T, H, W, heads, d), row-major, 16-byte
+ *     aligned base pointers.
+ *   - Return value: SKIPARSE_OK (0) or a negative skiparse_status.  Arguments
+ *     are validated before anything is launched; on error nothing is
+ *     enqueued and skiparse_last_error() describes the problem.
+ *   - Thread safety: the library keeps no state apart from a thread-local
+ *     error string.
+ */
+#ifndef SKIPARSE_H
+#define SKIPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKIPARSE_ABI_VERSION 1
+#define SKIPARSE_MAX_K 8
+
+typedef enum {
+  SKIPARSE_OK = 0,
+  SKIPARSE_EINVAL = -1,        /* bad argument: null or misaligned pointer, bad size */
+  SKIPARSE_EUNSUPPORTED = -2,  /* valid but not built: d not in {64, 128}, k > 8, ... */
+  SKIPARSE_EHIP = -3,          /* the HIP runtime reported an error at launch */
+  SKIPARSE_EWORKSPACE = -4     /* workspace missing or too small */
+} skiparse_status;
+
+typedef enum {
+  SKIPARSE_MODE_TOKEN = 0,     /* token-wise pattern */
+  SKIPARSE_MODE_GROUP = 1      /* group-wise pattern (ignored when k == 1) */
+} skiparse_mode;
+
+typedef enum {
+  SKIPARSE_F32 = 0,            /* fp32 in, fp32 out */
+  SKIPARSE_BF16 = 1,           /* bf16 in, bf16 out, fp32 accumulation */
+  SKIPARSE_FP8_E4M3 = 2        /* OCP e4m3 in (per-tensor scaled), bf16 out */
+} skiparse_dtype;
+
+/*
+ * Geometry of one attention call, filled by skiparse_plan_init.  Plain data:
+ * the caller owns it and may copy it.
+ *   Hp, Wp          H, W rounded up to a multiple of k*k (any-resolution rule)
+ *   sub_h, sub_w    local grid of a subsequence: Hp / k rows, Wp / k columns;
+ *                   every subsequence spans all T frames
+ *   sub_len_padded  T * sub_h * sub_w slots per subsequence
+ *   real_h[p]       real local rows of subsequences with row coordinate p
+ *   real_w[q]       real local columns of subsequences with column coordinate q
+ *                   The real tokens of subsequence s = p*k + q fill the prefix
+ *                   box [0,T) x [0,real_h[p]) x [0,real_w[q]) of its local grid.
+ *   pairs           computed (real x real, same subsequence) query-key pairs
+ *                   of a whole call: sum_s n_s^2 * B * heads; 4 * d * pairs
+ *                   is the call's algorithmic FLOP count
+ */
+typedef struct skiparse_plan {
+  int32_t abi;
+  int32_t B, T, H, W, heads, d, k, mode;
+  int32_t Hp, Wp;
+  int32_t sub_h, sub_w;
+  int32_t n_sub;
+  int32_t reserved0;
+  int64_t sub_len_padded;
+  int64_t pairs;
+  int32_t real_h[SKIPARSE_MAX_K];
+  int32_t real_w[SKIPARSE_MAX_K];
+} skiparse_plan;
+
+/* Returns SKIPARSE_ABI_VERSION. */
+int skiparse_abi_version(void);
+
+/*
+ * Fill *plan for tensors of shape (B, T, H, W, heads, d), sparsity factor k
+ * (1 <= k <= 8) and pattern mode (token- or group-wise, see the top of this
+ * file).  Host only, O(k^2).  Limits: every extent >= 1; T*Hp*Wp < 2^31
+ * (Hp, Wp the padded extents); heads*d < 2^31; B*T*H*W*heads*d < 4.6e18.  d outside {64, 128} is accepted here and refused
+ * by skiparse_attn_fwd.  Errors: SKIPARSE_EINVAL.
+ */
+int skiparse_plan_init(skiparse_plan* plan, int32_t B, int32_t T, int32_t H, int32_t W,
+                       int32_t heads, int32_t d, int32_t k, int32_t mode);
+
+/*
+ * Host index map (the rearrange of the core method, with the any-resolution
+ * padding): host_gather[s * sub_len_padded + j] = flat token index
+ * (t*H + h)*W + w held by slot j of subsequence s, slots enumerating the
+ * padded local grid (T, sub_h, sub_w) row-major, or -1 for a padded slot.
+ * host_gather: caller-owned host array of n_sub * sub_len_padded int32.
+ * Errors: SKIPARSE_EINVAL.
+ */
+int skiparse_plan_index_map(const skiparse_plan* plan, int32_t* host_gather);
+
+/*
+ * The same map, written on the device by the index function the attention
+ * kernels use to gather Q/K/V rows and scatter O rows.  dev_gather: device
+ * array of n_sub * sub_len_padded int32.  Errors: SKIPARSE_EINVAL,
+ * SKIPARSE_EHIP.
+ */
+int skiparse_index_map_device(const skiparse_plan* plan, int32_t* dev_gather, hipStream_t stream);
+
+/*
+ * Skiparse-2D attention forward (core method + method steps, see the top of
+ * this file): for every batch b, head and subsequence s in
+ * [sub_begin, sub_begin + sub_count) (sub_count == 0 means all n_sub and
+ * then needs sub_begin == 0), each
+ * real query token x of s gets
+ *     O[x] = sum_y softmax_y(softmax_scale * <Q[x], K[y]>) V[y]
+ * over the real tokens y of s.  Rows of O outside the run subsequences are
+ * not written.  Padded tokens are never read or written.
+ *   dtype             SKIPARSE_F32: q/k/v/o fp32.  SKIPARSE_BF16: q/k/v/o bf16.
+ *                     SKIPARSE_FP8_E4M3: q/k/v e4m3 bytes quantized per
+ *                     tensor (skiparse_quant_fp8), o bf16.
+ *   softmax_scale     <= 0 selects 1/sqrt(d)
+ *   dev_descale_qkv   FP8 only: device array of 3 fp32 {1/s_q, 1/s_k, 1/s_v}
+ *                     (the second element of each skiparse_quant_fp8 scale
+ *                     pair); NULL otherwise.  Q, K, V stand for code/s.
+ *   o                 must not overlap q, k or v.
+ * Supported: d in {64, 128} (F32 and BF16), d == 128 (FP8); 1 <= k <= 8.
+ * Errors: SKIPARSE_EINVAL, SKIPARSE_EUNSUPPORTED, SKIPARSE_EHIP.
+ */
+int skiparse_attn_fwd(const skiparse_plan* plan, skiparse_dtype dtype,
+                      const void* q, const void* k, const void* v, void* o,
+                      float softmax_scale, const float* dev_descale_qkv,
+                      int32_t sub_begin, int32_t sub_count, hipStream_t stream);
+
+/* Workspace bytes skiparse_quant_fp8 needs for numel elements. */
+size_t skiparse_quant_fp8_workspace_bytes(int64_t numel);
+
+/*
+ * Per-tensor 8-bit quantization with the pages' scale rule
+ * scale = fp8_max / (amax + eps), amax = max |x| over the whole tensor, one
+ * scale per tensor and no finer blocks (OSP-Next summary, 方法步骤详情 method
+ * steps).  The pages' format (HiF8) is replaced by OCP e4m3 with
+ * fp8_max = 448.  Every step is IEEE fp32: scale = fp8_max / (amax + eps);
+ * y[i] = e4m3(x[i] * scale), rounded to nearest even and saturated to +-448.
+ *   x          device, numel elements of x_dtype (SKIPARSE_BF16 or SKIPARSE_F32)
+ *   y          device, numel bytes
+ *   dev_scale  device, 2 fp32: {scale, 1/scale}
+ *   workspace  device, >= skiparse_quant_fp8_workspace_bytes(numel) bytes,
+ *              contents need not be initialized; it is overwritten
+ * Inputs must be finite.  Errors: SKIPARSE_EINVAL, SKIPARSE_EWORKSPACE,
+ * SKIPARSE_EHIP.
+ */
+int skiparse_quant_fp8(const void* x, skiparse_dtype x_dtype, int64_t numel, uint8_t* y,
+                       float* dev_scale, float fp8_max, float eps,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Description of the last error on the calling thread ("" if none); valid
+ * until the next library call on that thread. */
+const char* skiparse_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKIPARSE_H */

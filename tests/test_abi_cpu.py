@@ -1,0 +1,178 @@
+"""The C ABI on the host (no GPU needed): the library loads and exports every
+entry point include/skiparse.h declares; the host plan and host index map
+match the oracle exactly; invalid arguments are refused with the documented
+status codes before anything reaches the GPU; the fast division in the index
+function is exact."""
+
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import fixed_pattern_sparse_amd as sk
+from oracle import skiparse_ref as ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skiparse.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(skiparse_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(sk.EXPORTED)
+    L = sk.lib()
+    for name in names:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", sk.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    exported = set(re.findall(r"\bT (skiparse_\w+)", out))
+    assert set(names) <= exported
+    assert sk.skiparse_abi_version() == 1
+
+
+SHAPES = [
+    (1, 2, 8, 8, 2, 64), (1, 21, 45, 80, 40, 128), (2, 21, 48, 80, 40, 128), (1, 21, 32, 52, 12, 128),
+    (1, 1, 1, 1, 1, 64), (3, 2, 7, 13, 3, 128), (1, 5, 17, 3, 1, 64), (1, 1, 100, 37, 2, 64),
+]
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_plan_matches_oracle(shape, k, mode):
+    B, T, H, W, nh, d = shape
+    p = sk.skiparse_plan_init(B, T, H, W, nh, d, k, mode)
+    o = ref.make_plan(B, T, H, W, nh, d, k, mode)
+    assert (p.Hp, p.Wp, p.sub_h, p.sub_w, p.n_sub, p.sub_len_padded) == (o.Hp, o.Wp, o.sub_h, o.sub_w, o.n_sub, o.sub_len_padded)
+    assert list(p.real_h)[:k] == o.real_h and list(p.real_w)[:k] == o.real_w
+    assert p.pairs == o.pairs
+    assert p.mode == o.mode
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 7, 8])
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("T,H,W", [(1, 4, 4), (2, 8, 8), (1, 3, 5), (3, 9, 7), (2, 21, 45), (1, 45, 80),
+                                   (2, 64, 65), (1, 1, 1), (4, 13, 2)])
+def test_host_index_map_bit_exact(T, H, W, k, mode):
+    p = sk.skiparse_plan_init(1, T, H, W, 1, 64, k, mode)
+    np.testing.assert_array_equal(sk.skiparse_plan_index_map(p), ref.gather_map(T, H, W, k, mode))
+
+
+def test_host_index_map_at_720p_shape():
+    for k in (2, 4):
+        for mode in (0, 1):
+            p = sk.skiparse_plan_init(1, 21, 45, 80, 40, 128, k, mode)
+            np.testing.assert_array_equal(sk.skiparse_plan_index_map(p), ref.gather_map(21, 45, 80, k, mode))
+
+
+@pytest.mark.parametrize("args", [
+    (0, 1, 1, 1, 1, 64, 2, 0), (1, 1, 1, 1, 1, 64, 0, 0), (1, 1, 1, 1, 1, 64, 9, 0),
+    (1, 1, 1, 1, 1, 64, 2, 2), (1, -1, 4, 4, 1, 64, 2, 0), (1, 1, 70000, 70000, 1, 64, 1, 0),
+])
+def test_plan_init_rejects(args):
+    with pytest.raises(sk.SkiparseError) as e:
+        sk.skiparse_plan_init(*args)
+    assert e.value.code == sk.EINVAL
+    assert sk.skiparse_last_error()
+
+
+def _attn_code(plan, dtype=sk.BF16, q=0x1000, k=0x100000000, v=0x200000000, o=0x300000000, scale=0.0,
+               descale=None, sb=0, sc=0):
+    import ctypes
+    return sk.lib().skiparse_attn_fwd(ctypes.byref(plan), dtype, q, k, v, o, scale, descale, sb, sc, None)
+
+
+def test_attn_fwd_argument_errors():
+    """Each call below fails validation, so nothing is launched (the pointers
+    are never dereferenced)."""
+    import ctypes
+    p = sk.skiparse_plan_init(1, 2, 8, 8, 2, 64, 2, 0)
+    assert _attn_code(p, q=0) == sk.EINVAL
+    assert _attn_code(p, q=0x1008) == sk.EINVAL                       # misaligned
+    assert _attn_code(p, o=0x1000 + 64) == sk.EINVAL                  # o overlaps q
+    assert _attn_code(p, dtype=7) == sk.EINVAL
+    assert _attn_code(p, sb=1, sc=0) == sk.EINVAL
+    assert _attn_code(p, sb=3, sc=2) == sk.EINVAL
+    assert _attn_code(p, sb=-1, sc=1) == sk.EINVAL
+    assert _attn_code(p, scale=float("inf")) == sk.EINVAL
+    assert _attn_code(p, descale=0x5000) == sk.EINVAL                 # descale only for FP8
+    assert _attn_code(p, dtype=sk.FP8_E4M3) == sk.EUNSUPPORTED        # FP8 needs d = 128
+    p128 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 128, 2, 0)
+    assert _attn_code(p128, dtype=sk.FP8_E4M3) == sk.EINVAL           # no descale pointer
+    p96 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 96, 2, 0)
+    assert _attn_code(p96) == sk.EUNSUPPORTED
+    bad = sk.skiparse_plan_init(1, 2, 8, 8, 2, 64, 2, 0)
+    bad.Hp = 4                                                        # tampered plan
+    assert _attn_code(bad) == sk.EINVAL
+    assert "modified" in sk.skiparse_last_error()
+    assert sk.lib().skiparse_attn_fwd(None, 1, 0x1000, 0x2000, 0x3000, 0x4000, 0.0, None, 0, 0, None) == sk.EINVAL
+
+
+def test_quant_argument_errors():
+    L = sk.lib()
+    n = 1000
+    need = sk.skiparse_quant_fp8_workspace_bytes(n)
+    assert need >= 4
+    assert L.skiparse_quant_fp8(0x1000, sk.BF16, n, 0x100000, 0x200000, 448.0, 1e-12, 0x300000, need - 4, None) == sk.EWORKSPACE
+    assert L.skiparse_quant_fp8(0x1000, sk.BF16, n, 0x100000, 0x200000, 448.0, 1e-12, None, need, None) == sk.EWORKSPACE
+    assert L.skiparse_quant_fp8(0x1000, sk.FP8_E4M3, n, 0x100000, 0x200000, 448.0, 1e-12, 0x300000, need, None) == sk.EINVAL
+    assert L.skiparse_quant_fp8(0x1000, sk.BF16, 0, 0x100000, 0x200000, 448.0, 1e-12, 0x300000, need, None) == sk.EINVAL
+    assert L.skiparse_quant_fp8(0x1001, sk.BF16, n, 0x100000, 0x200000, 448.0, 1e-12, 0x300000, need, None) == sk.EINVAL
+    assert L.skiparse_quant_fp8(0x1000, sk.BF16, n, 0x1100, 0x200000, 448.0, 1e-12, 0x300000, need, None) == sk.EINVAL
+    assert L.skiparse_quant_fp8(0x1000, sk.BF16, n, 0x100000, 0x200000, -1.0, 1e-12, 0x300000, need, None) == sk.EINVAL
+    assert sk.skiparse_last_error()
+
+
+def test_index_map_device_argument_errors():
+    import ctypes
+    p = sk.skiparse_plan_init(1, 2, 8, 8, 2, 64, 2, 0)
+    assert sk.lib().skiparse_index_map_device(ctypes.byref(p), None, None) == sk.EINVAL
+    assert sk.lib().skiparse_index_map_device(ctypes.byref(p), 0x1002, None) == sk.EINVAL
+
+
+FASTDIV_PROBE = r"""
+#include <cstdio>
+#include <cstdint>
+#include <random>
+#include "geom.h"
+int main() {
+  std::mt19937_64 rng(7);
+  const uint32_t divs[] = {1, 2, 3, 5, 7, 8, 9, 24, 40, 80, 960, 1000, 65537, 123456789, 2147483647u};
+  for (uint32_t d : divs) {
+    skiparse::FastDiv f = skiparse::make_fastdiv(d);
+    for (int i = 0; i < 200000; ++i) {
+      uint32_t n = (uint32_t)(rng() & 0x7FFFFFFFu);
+      if (i < 1000) n = i;
+      if (i >= 1000 && i < 2000) n = 0x7FFFFFFFu - (i - 1000);
+      if (skiparse::fdiv(n, f) != n / d) { printf("FAIL %u / %u\n", n, d); return 1; }
+    }
+    for (uint32_t m = 1; m < 4096; ++m) {   // around multiples of d
+      uint64_t x = (uint64_t)d * m;
+      for (int e = -1; e <= 1; ++e) {
+        uint64_t n = x + e;
+        if (n >= 0x80000000ull) continue;
+        if (skiparse::fdiv((uint32_t)n, f) != (uint32_t)n / d) { printf("FAIL %llu / %u\n", (unsigned long long)n, d); return 1; }
+      }
+    }
+  }
+  printf("OK\n");
+  return 0;
+}
+"""
+
+
+def test_fastdiv_exact(tmp_path):
+    src = tmp_path / "fd.cpp"
+    src.write_text(FASTDIV_PROBE)
+    exe = tmp_path / "fd"
+    inc = os.path.join(ROOT, "fixed_pattern_sparse_amd", "csrc")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", inc, str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "OK", r.stdout
