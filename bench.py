@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the Skiparse-2D attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 720p_5s]
+
+A step is one token-wise layer followed by one group-wise layer (the pattern
+alternation of the method) over the workload's Q, K, V, already resident in
+HBM.  Printed as ONE JSON line: TFLOP/s counting only computed (real x real,
+same subsequence) pairs, ms per step, the roofline of the attention kernel
+(average launch duration from HIP events on the launch stream), the oracle's
+CPU baseline on a bounded sample, and extras: ms per layer, the same kernel at
+k = 1 (full attention) and the fp8 path.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+HBM_GBS = 8000.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_fwd_bf16_720p_5s_pmc.md")
+KERNEL_SOURCES = ["fixed_pattern_sparse_amd/csrc/attn_bf16.hip", "fixed_pattern_sparse_amd/csrc/geom.h",
+                  "fixed_pattern_sparse_amd/csrc/internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch recorded from rocprofv3 counters, if they were taken
+    on the current kernel source (else None)."""
+    if workload != "720p_5s" or not os.path.exists(PROFILE_PMC):
+        return None
+    text = open(PROFILE_PMC).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(workload, cpu_inputs, budget_s=20.0):
+    """The oracle's fp32 numpy/BLAS algorithm on a bounded sample of units
+    (b = 0, heads 0.., every subsequence of both patterns), scaled by pairs."""
+    from oracle import cpu_baseline as cb
+    B, T, H, W, nh, d = workload.shape
+    N = T * H * W
+    q, k, v = (t.float().numpy().reshape(B, N, nh, d) for t in cpu_inputs)
+    secs = 0.0
+    pairs = 0
+    units = 0
+    heads_done = 0
+    for h in range(nh):
+        for mode in (0, 1):
+            us = [(0, h, s) for s in range(workload.k * workload.k)]
+            dt, pr = cb.time_sample(q, k, v, T, H, W, workload.k, mode, us)
+            secs += dt
+            pairs += pr
+            units += len(us)
+        heads_done += 1
+        if secs > budget_s:
+            break
+    tflops = 4 * d * pairs / secs / 1e12
+    return {
+        "value": round(tflops, 6),
+        "unit": "TFLOP/s",
+        "cores": cb.blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{units} (batch, head, subsequence) units = heads 0-{heads_done - 1} of batch 0, all "
+                   f"{workload.k * workload.k} subsequences of both patterns; {pairs:.4g} pairs in "
+                   f"{secs:.1f} s, fp32 numpy/BLAS; TFLOP/s scales exactly by pair count"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p_5s")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path; "
+              "the sharding design is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fixed_pattern_sparse_amd as sk
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("the timed step uses a bf16 workload")
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    t0 = time.time()
+    cpu = wl.make_inputs(w)
+    q, k, v = (t.to("cuda") for t in cpu)
+    o_tok = torch.empty_like(q)
+    o_grp = torch.empty_like(q)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    B, T, H, W, nh, d = w.shape
+    p_tok = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, sk.MODE_TOKEN)
+    p_grp = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, sk.MODE_GROUP)
+    flops_step = p_tok.flops + p_grp.flops
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sk.skiparse_attn_fwd(p_tok, sk.BF16, q, k, v, o_tok, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+            ev[2].record(stream)
+        sk.skiparse_attn_fwd(p_grp, sk.BF16, q, k, v, o_grp, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_step = elapsed * 1e3 / args.steps
+    launch_ms = []
+    for ev in events:
+        launch_ms.append(ev[0].elapsed_time(ev[1]))
+        launch_ms.append(ev[2].elapsed_time(ev[3]))
+    avg_launch_ms = float(np.mean(launch_ms))
+    achieved = (flops_step / 2) / (avg_launch_ms * 1e-3) / 1e12
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step, kernel avg {avg_launch_ms:.3f} ms/launch",
+          file=sys.stderr, flush=True)
+
+    traffic = recorded_traffic(args.workload)
+    result = {
+        "metric": "Skiparse-2D attn fwd TFLOP/s + ms/layer, 720P-5s shape, 1 MI355X",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "H": H, "W": W, "heads": nh, "d": d, "k": w.k,
+                   "padded_H": p_tok.Hp, "padded_W": p_tok.Wp, "outlier_channels": w.outliers,
+                   "step": "token-wise layer + group-wise layer", "flop_per_step": flops_step},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,4,1>",
+                     "avg_launch_ms": round(avg_launch_ms, 4)},
+    }
+    extras = {"ms_per_layer": round(ms_step / 2, 4)}
+
+    if not args.no_extras:
+        # same kernel at k = 1 (full attention, the hybrid model's full layers)
+        p1 = sk.skiparse_plan_init(B, T, H, W, nh, d, 1, sk.MODE_TOKEN)
+        o1 = torch.empty_like(q)
+        sk.skiparse_attn_fwd(p1, sk.BF16, q, k, v, o1, stream=stream)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(3):
+            sk.skiparse_attn_fwd(p1, sk.BF16, q, k, v, o1, stream=stream)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        k1_ms = e[0].elapsed_time(e[1]) / 3
+        extras["k1_ms_per_layer"] = round(k1_ms, 3)
+        extras["k1_tflops"] = round(p1.flops / (k1_ms * 1e-3) / 1e12, 3)
+        extras["speedup_vs_k1"] = round(k1_ms / avg_launch_ms, 3)
+        del o1
+    result["extras"] = extras
+
+    if not args.no_cpu_baseline:
+        print("# cpu baseline ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, cpu)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
