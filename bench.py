@@ -175,7 +175,7 @@ def main():
                    "step": "token-wise layer + group-wise layer", "flop_per_step": flops_step},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,4,1>",
+                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128, true>",
                      "avg_launch_ms": round(avg_launch_ms, 4)},
     }
     extras = {"ms_per_layer": round(ms_step / 2, 4)}

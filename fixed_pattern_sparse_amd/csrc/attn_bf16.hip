@@ -6,36 +6,48 @@
 // token-wise or group-wise rearrange, written back in the original layout;
 // padding from the any-resolution rule is never computed.
 //
-// Work decomposition: one work-group per (batch, head, subsequence, tile of BM
-// queries).  Each wave owns QB blocks of 32 queries.  Keys are streamed in
-// tiles of 64 rows through double-buffered LDS; rows are gathered straight
-// from the (B, T, H, W, heads, d) tensors by the index function (no permuted
-// copy), with direct global->LDS loads.
+// Work decomposition: one work-group of 8 waves per (batch, head,
+// subsequence, tile of 256 queries); each wave owns 32 queries.  Keys are
+// streamed in tiles of 64 rows through double-buffered LDS.  Each iteration
+// first issues the global loads of the next K/V tile into registers (rows
+// gathered straight from the (B, T, H, W, heads, d) tensors, no permuted
+// copy), computes on the current tile, then writes the staged rows to the
+// other LDS buffer with 16-byte stores.  Plain loads and LDS stores measured
+// well ahead of direct global->LDS loads for this access pattern.
 //
 // Per 64-key tile and 32-query block:
-//   S^T = K Q^T   8 x v_mfma_f32_32x32x16_bf16 per 32 keys (d = 128); the
-//                 transposed orientation leaves one query per lane, so row
-//                 statistics need one cross-half swap and no shuffles;
+//   S^T = K Q^T    v_mfma_f32_32x32x16_bf16; the transposed orientation
+//                  leaves one query per lane, so row statistics need one
+//                  cross-half swap and no shuffles;
 //   online softmax in the log2 domain with a lazily raised running max: the
-//                 accumulator is rescaled only when a tile's max exceeds the
-//                 running max by more than 2^8, which keeps p <= 256 and the
-//                 result exact (O and l share the same offset);
+//                  accumulator is rescaled only when a tile's max exceeds the
+//                  running max by more than 2^8, which keeps p <= 256 and the
+//                  result exact (O and l share the same offset);
 //   O^T += V^T P^T  V^T comes from row-major V in LDS through
-//                 ds_read_b64_tr_b16, P^T stays in registers as bf16.
+//                  ds_read_b64_tr_b16; P^T stays in registers as bf16.
 #include "internal.h"
 
 namespace skiparse {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-constexpr int kBN = 64;          // keys per tile
-constexpr float kTau = 8.0f;     // slack of the running max, log2 units
+constexpr int kBN = 64;            // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBM = kWaves * 32;   // queries per work-group
+constexpr float kTau = 8.0f;       // slack of the running max, log2 units
+constexpr int kTileBytes = kBN * 128 * 2;
+constexpr int kRowCap = 2048;      // capacity of the (t, h') row table
+constexpr int kColCap = 512;       // capacity of the w' column table
 
-typedef __attribute__((address_space(3))) void lds_void;
+__shared__ __attribute__((aligned(16))) char gKV[4 * kTileBytes];   // K0 K1 V0 V1
+__shared__ int32_t gRowBase[kRowCap];   // (t*H + h) * W for local row th = t*hr + h'
+__shared__ int32_t gColMap[kColCap];    // w for local column w'
 
 __device__ __forceinline__ int xcd_remap(int i, int n) {
   // Work-groups are handed to the 8 XCDs round-robin.  Give each XCD one
@@ -49,30 +61,31 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 
 template <int D>
 struct Layout {
-  static constexpr int CH = D / 8;           // 16-byte chunks per row
-  static constexpr int ROWB = D * 2;         // bytes per row
-  static constexpr int TILEB = kBN * ROWB;   // bytes per K or V tile
-  // XOR swizzles of the chunk index: K rows are read 32 at a time at one
-  // chunk (ds_read_b128), V rows 8 at a time over 4 chunks (ds_read_b64_tr_b16).
+  static constexpr int CH = D / 8;             // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;           // bytes per row
+  static constexpr int CPT = kBN * CH / kThreads;  // chunks per thread per tile and matrix
+  static constexpr int RSTEP = kThreads / CH;  // row distance between a thread's chunks
+  // XOR swizzles of the 16-byte chunk index: K rows are read 32 at a time at
+  // one chunk (ds_read_b128), V rows 8 at a time over 4 chunks
+  // (ds_read_b64_tr_b16); both patterns hit every bank group evenly.
   __device__ static int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   __device__ static int vswz(int r) { return D == 128 ? ((r & 3) << 2) : ((r & 1) << 2); }
 };
 
-template <int D, int NW, int QB>
-__global__ void __launch_bounds__(NW * 64)
+// FAST: token rows come from the LDS tables, offsets are 32-bit from a scalar
+// base (needs T*H*W < 2^24, heads*d*2 < 2^24, a batch sample's tensor < 4 GB
+// and table room).  Otherwise the index function is evaluated per row.
+template <int D, bool FAST>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const AttnArgs a) {
   using L = Layout<D>;
-  constexpr int BM = NW * QB * 32;
   constexpr int KK = D / 16;                 // MFMA steps over d
   constexpr int DB = D / 32;                 // 32-wide d blocks of O
-  constexpr int LOADS = kBN * L::CH / 64;    // 1 KB load instructions per tile and matrix
-  constexpr int LPW = LOADS / NW;            // ... per wave
-  static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
+  static_assert(L::CPT >= 1 && L::CPT * kThreads == kBN * L::CH, "tile chunks must split evenly");
 
-  __shared__ __attribute__((aligned(16))) char smem[4 * L::TILEB];   // K0 K1 V0 V1
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int hl = lane >> 5;                  // lane half
   const int l32 = lane & 31;
 
@@ -88,78 +101,111 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   const int qtile = rem - sg.tile0;
   const int n = sg.n;
   const int nkv = (n + kBN - 1) / kBN;
+  const int wr = (int)sg.div_w.d;
+  const int th_end = n / wr;                 // T * hr
 
   const int64_t base = (int64_t)b * a.batch_stride + (int64_t)head * D;
   const __bf16* __restrict__ qp = (const __bf16*)a.q + base;
-  const __bf16* __restrict__ kp = (const __bf16*)a.k + base;
-  const __bf16* __restrict__ vp = (const __bf16*)a.v + base;
+  const char* __restrict__ kb = (const char*)((const __bf16*)a.k + base);
+  const char* __restrict__ vb = (const char*)((const __bf16*)a.v + base);
   __bf16* __restrict__ op = (__bf16*)a.o + base;
   const int64_t rs = a.row_stride;
+  const uint32_t rsb = (uint32_t)a.row_stride * 2u;
 
-  // ---- K/V tile loader: direct global -> LDS, 16 B per lane -----------------
-  // Load instruction u of a tile writes LDS bytes [u*1024, u*1024+1024): row
-  // (u*64 + lane) / CH, chunk slot (u*64 + lane) % CH, holding global chunk
-  // slot ^ swizzle(row).
-  auto issue_tile = [&](int it, int buf) {
+  // ---- row tables (FAST) ---------------------------------------------------
+  if constexpr (FAST) {
+    const int hr = th_end / a.g.T;
+    for (int x = tid; x < th_end; x += kThreads) {
+      const int t = x / hr;
+      const int hh = (int)axis_of_local((uint32_t)(x - t * hr), (uint32_t)sg.p, a.g);
+      gRowBase[x] = (t * a.g.H + hh) * a.g.W;
+    }
+    for (int x = tid; x < wr; x += kThreads) gColMap[x] = (int)axis_of_local((uint32_t)x, (uint32_t)sg.q, a.g);
+    __syncthreads();
+  }
+
+  // ---- loader: thread owns chunk slot tid % CH of rows tid / CH + i*RSTEP ----
+  // For FAST each row walks through the tiles by its compact index
+  // j = tile*64 + r = th*wr + w', advanced by 64 = dth*wr + dw per tile.
+  const int lslot = tid % L::CH;
+  int st_th[L::CPT], st_w[L::CPT];
+  const int dth = kBN / wr, dw = kBN - (kBN / wr) * wr;
+  int tok_last = 0;
+  if constexpr (FAST) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int u = wave * LPW + i;
-      const int lin = u * 64 + lane;
-      const int row = lin / L::CH;
-      const int slot = lin % L::CH;
-      int j = it * kBN + row;
-      j = j < n ? j : n - 1;
-      const int64_t off = (int64_t)token_of((uint32_t)j, sg, a.g) * rs;
-      const int ck = slot ^ L::kswz(row);
-      const int cv = slot ^ L::vswz(row);
-      __builtin_amdgcn_global_load_lds((const void*)(kp + off + ck * 8),
-                                       (lds_void*)(smem + buf * L::TILEB + u * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vp + off + cv * 8),
-                                       (lds_void*)(smem + (2 + buf) * L::TILEB + u * 1024), 16, 0, 0);
+    for (int i = 0; i < L::CPT; ++i) {
+      const int r = tid / L::CH + i * L::RSTEP;
+      st_th[i] = r / wr;
+      st_w[i] = r - st_th[i] * wr;
+    }
+    const int jl = n - 1;
+    const int tl = jl / wr;
+    tok_last = gRowBase[tl] + gColMap[jl - tl * wr];
+  }
+  struct Stage { uint4 k[L::CPT], v[L::CPT]; };   // staged chunks of a tile
+  auto fetch = [&](int tile) -> Stage {
+    Stage sgd;
+#pragma unroll
+    for (int i = 0; i < L::CPT; ++i) {
+      int tok;
+      if constexpr (FAST) {
+        tok = st_th[i] < th_end ? gRowBase[st_th[i]] + gColMap[st_w[i]] : tok_last;
+        st_w[i] += dw;
+        const int cy = st_w[i] >= wr;
+        st_w[i] -= cy ? wr : 0;
+        st_th[i] += dth + cy;
+        const uint32_t off = __umul24((uint32_t)tok, rsb) + (uint32_t)(lslot * 16);
+        sgd.k[i] = *(const uint4*)(kb + off);
+        sgd.v[i] = *(const uint4*)(vb + off);
+      } else {
+        int j = tile * kBN + tid / L::CH + i * L::RSTEP;
+        j = j < n ? j : n - 1;
+        tok = (int)token_of((uint32_t)j, sg, a.g);
+        const int64_t off = (int64_t)tok * rs * 2 + lslot * 16;
+        sgd.k[i] = *(const uint4*)(kb + off);
+        sgd.v[i] = *(const uint4*)(vb + off);
+      }
+    }
+    return sgd;
+  };
+  auto stash = [&](const Stage& sgd, int buf) {
+#pragma unroll
+    for (int i = 0; i < L::CPT; ++i) {
+      const int r = tid / L::CH + i * L::RSTEP;
+      *(uint4*)(gKV + buf * kTileBytes + r * L::ROWB + (lslot ^ L::kswz(r)) * 16) = sgd.k[i];
+      *(uint4*)(gKV + (2 + buf) * kTileBytes + r * L::ROWB + (lslot ^ L::vswz(r)) * 16) = sgd.v[i];
     }
   };
 
-  issue_tile(0, 0);
+  const Stage first = fetch(0);
 
   // ---- Q fragments (B operand of S^T = K Q^T) ------------------------------
-  bf16x8 qf[QB][KK];
-  int64_t qoff[QB];
-  bool qok[QB];
+  bf16x8 qf[KK];
+  const int jq = qtile * kBM + wave * 32 + l32;
+  const bool qok = jq < n;
+  const int64_t qoff = (int64_t)token_of((uint32_t)(qok ? jq : n - 1), sg, a.g) * rs;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int j = qtile * BM + (wave * QB + qb) * 32 + l32;
-    qok[qb] = j < n;
-    const int jc = j < n ? j : n - 1;
-    qoff[qb] = (int64_t)token_of((uint32_t)jc, sg, a.g) * rs;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qf[qb][kk] = *(const bf16x8*)(qp + qoff[qb] + kk * 16 + hl * 8);
-  }
+  for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const bf16x8*)(qp + qoff + kk * 16 + hl * 8);
 
-  floatx16 acc[QB][DB];
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[qb][db] = floatx16{};
-  }
-  const float c = a.scale_log2;
-
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's tile-0 loads landed
+  stash(first, 0);
   __syncthreads();
 
-  for (int it = 0; it < nkv; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nkv) issue_tile(it + 1, buf ^ 1);
-    const char* sK = smem + buf * L::TILEB;
-    const char* sV = smem + (2 + buf) * L::TILEB;
-
-    // S^T = K Q^T : two 32-key blocks
-    floatx16 s[QB][2];
+  floatx16 acc[DB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) { s[qb][0] = floatx16{}; s[qb][1] = floatx16{}; }
+  for (int db = 0; db < DB; ++db) acc[db] = floatx16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+
+  for (int j = 0; j < nkv; ++j) {
+    const int buf = j & 1;
+    const bool more = j + 1 < nkv;
+    Stage nxt;
+    if (more) nxt = fetch(j + 1);   // in flight during this tile's compute
+    const char* sK = gKV + buf * kTileBytes;
+    const char* sV = gKV + (2 + buf) * kTileBytes;
+
+    // S^T = K Q^T
+    floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -167,64 +213,59 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
         const int row = mb * 32 + l32;
         const int ch = (2 * kk + hl) ^ L::kswz(row);
         const bf16x8 kf = *(const bf16x8*)(sK + row * L::ROWB + ch * 16);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[qb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][kk], s[qb][mb], 0, 0, 0);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[mb], 0, 0, 0);
       }
     }
 
-    // keys past the end of the subsequence (last tile only)
-    if ((it + 1) * kBN > n) {
+    // online softmax
+    if ((j + 1) * kBN > n) {   // keys past the end of the subsequence
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = it * kBN + mb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-          if (key >= n) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][mb][i] = -INFINITY;
-          }
+          const int key = j * kBN + mb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+          if (key >= n) s[mb][i] = -INFINITY;
         }
     }
-
-    // online softmax; P^T packed to bf16 as the B operand of the PV product
-    bf16x8 pk[QB][2][2];
+    float mx = s[0][0];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[qb][0][0];
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[qb][0][i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][1][i]);
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      const float mx2 = mx * c;
-      if (__builtin_amdgcn_ballot_w64(mx2 > m_run[qb] + kTau)) {
-        const float mnew = fmaxf(m_run[qb], mx2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
-        m_run[qb] = mnew;
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
-      }
-      const float mneg = -m_run[qb];
-      float lsum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][mb][cc * 8 + e], c, mneg));
-            lsum += p;
-            pk[qb][mb][cc][e] = (__bf16)p;
-          }
-      l_run[qb] += lsum;
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
+    const float mx2 = mx * c;
+    if (__builtin_amdgcn_ballot_w64(mx2 > m_run + kTau)) {
+      // rare: raise the running max and rescale
+      const float mnew = fmaxf(m_run, mx2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      m_run = mnew;
+      l_run *= alpha;
+      // an fma with a zero addend, not a multiply: this keeps the compiler
+      // from folding the rare rescale into an every-tile multiply
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] = __builtin_fmaf(acc[db][i], alpha, 0.0f);
+    }
+    const float mneg = -m_run;
+    bf16x8 pk[2][2];
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][cc * 8 + 2 * e], c, mneg));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][cc * 8 + 2 * e + 1], c, mneg));
+          lsum[mb * 2 + cc] += p0 + p1;
+          pk[mb][cc][2 * e] = (__bf16)p0;
+          pk[mb][cc][2 * e + 1] = (__bf16)p1;
+        }
+    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
     // O^T += V^T P^T
 #pragma unroll
@@ -240,55 +281,62 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
             const int col = db * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;   // elements
             const int ch = (col >> 3) ^ L::vswz(row);
             part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) shortx4*)(sV + row * L::ROWB + ch * 16 + (col & 7) * 2));
+                (lds_shortx4*)(sV + row * L::ROWB + ch * 16 + (col & 7) * 2));
           }
           bf16x8 vf;
           __builtin_memcpy(&vf, part, 16);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[qb][mb][cc], acc[qb][db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[mb][cc], acc[db], 0, 0, 0);
         }
       }
     }
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next tile landed in LDS
+    if (more) stash(nxt, buf ^ 1);   // the other buffer was last read before the previous barrier
     __syncthreads();
   }
 
   // ---- normalize and scatter back to the original token rows ---------------
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float inv = 1.0f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+  if (qok) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[qb]), __float_as_uint(l_run[qb]), false, false);
-    const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const float inv = 1.0f / l;
-    if (qok[qb]) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 v4;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[qb][db][g4 * 4 + e] * inv);
-          *(bf16x4*)(op + qoff[qb] + db * 32 + g4 * 8 + hl * 4) = v4;
-        }
-    }
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][g4 * 4 + e] * inv);
+        *(bf16x4*)(op + qoff + db * 32 + g4 * 8 + hl * 4) = v4;
+      }
   }
 }
 
-template <int D, int NW, int QB>
-hipError_t launch_cfg(AttnArgs a, int B, hipStream_t stream) {
-  constexpr int BM = NW * QB * 32;
-  assign_tiles(a, B, BM);
+template <int D>
+hipError_t launch_d(AttnArgs a, int B, hipStream_t stream) {
+  assign_tiles(a, B, kBM);
   if (a.total_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, QB>), dim3(a.total_tiles), dim3(NW * 64), 0, stream, a);
+  // the fast path needs 24-bit tokens and row strides, 32-bit offsets per
+  // batch sample, and room for the row tables of every run subsequence
+  const int64_t tokens = (int64_t)a.g.T * a.g.H * a.g.W;
+  const int64_t rsb = (int64_t)a.row_stride * 2;
+  bool fast = tokens < (1 << 24) && rsb < (1 << 24) && tokens * rsb < (int64_t(1) << 32);
+  for (int i = 0; i < a.n_run && fast; ++i) {
+    const SubGeom& s = a.sub[i];
+    if (s.n == 0) continue;
+    const int64_t th = s.n / (int64_t)s.div_w.d;
+    fast = th <= kRowCap && (int64_t)s.div_w.d <= kColCap;
+  }
+  if (fast)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(AttnArgs a, int B, int d, hipStream_t stream) {
-  if (d == 128) return launch_cfg<128, 4, 1>(a, B, stream);
-  return launch_cfg<64, 4, 1>(a, B, stream);
+  if (d == 128) return launch_d<128>(a, B, stream);
+  return launch_d<64>(a, B, stream);
 }
 
 }  // namespace skiparse
