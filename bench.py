@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HBM_GBS = 8000.0
+COPY_BYTES = 1 << 30          # calibration copy of the traffic run
 PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_fwd_bf16_720p_5s_pmc.md")
 KERNEL_SOURCES = ["fixed_pattern_sparse_amd/csrc/attn_bf16.hip", "fixed_pattern_sparse_amd/csrc/geom.h",
                   "fixed_pattern_sparse_amd/csrc/internal.h"]
@@ -96,6 +97,9 @@ def main():
     ap.add_argument("--workload", default="720p_5s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="for rocprofv3 --pmc: one 1 GiB copy kernel (calibration), then one token-wise and "
+                         "one group-wise layer, no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path; "
@@ -120,6 +124,19 @@ def main():
     print(f"# inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     B, T, H, W, nh, d = w.shape
+    if args.traffic_run:
+        # a plain elementwise copy of known size: reads and writes COPY_BYTES
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.add(src, 0.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        for mode in (sk.MODE_TOKEN, sk.MODE_GROUP):
+            plan = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, mode)
+            sk.skiparse_attn_fwd(plan, sk.BF16, q, k, v, o_tok, stream=stream)
+        torch.cuda.synchronize()
+        print("# traffic run done", file=sys.stderr, flush=True)
+        return
     p_tok = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, sk.MODE_TOKEN)
     p_grp = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, sk.MODE_GROUP)
     flops_step = p_tok.flops + p_grp.flops
@@ -196,6 +213,40 @@ def main():
         extras["k1_tflops"] = round(p1.flops / (k1_ms * 1e-3) / 1e12, 3)
         extras["speedup_vs_k1"] = round(k1_ms / avg_launch_ms, 3)
         del o1
+        # fp8 path on the same shape: per-tensor e4m3 quantization of Q, K, V
+        # (scale = 448 / (amax + 1e-12)) then the e4m3 kernel, k = 2 and k = 4
+        scales = torch.empty((3, 2), dtype=torch.float32, device="cuda")
+        codes = [sk.quantize_fp8(t, scale_out=scales[i])[0] for i, t in enumerate((q, k, v))]
+        o8 = torch.empty_like(q)
+        fp8 = {}
+        for kf in (2, 4):
+            for mode, name in ((sk.MODE_TOKEN, "token"), (sk.MODE_GROUP, "group")):
+                pl = sk.skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
+                sk.skiparse_attn_fwd(pl, sk.FP8_E4M3, *codes, o8, descale_qkv=scales, stream=stream)
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(stream)
+                for _ in range(5):
+                    sk.skiparse_attn_fwd(pl, sk.FP8_E4M3, *codes, o8, descale_qkv=scales, stream=stream)
+                e[1].record(stream)
+                torch.cuda.synchronize()
+                ms = e[0].elapsed_time(e[1]) / 5
+                fp8[f"k{kf}_{name}"] = {"ms": round(ms, 3), "tflops": round(pl.flops / (ms * 1e-3) / 1e12, 2),
+                                        "frac_fp8_peak": round(pl.flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4)}
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(3):
+            for i, t in enumerate((q, k, v)):
+                sk.quantize_fp8(t, scale_out=scales[i])
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        qms = e[0].elapsed_time(e[1]) / 3
+        # algorithmic HBM bytes of quantizing the three tensors: amax pass reads
+        # 2 B/elt, the cast reads 2 B/elt and writes 1 B/elt
+        qbytes = 3 * q.numel() * 5
+        fp8["quantize_qkv"] = {"ms": round(qms, 3), "GBps": round(qbytes / (qms * 1e-3) / 1e9, 1),
+                               "frac_hbm_peak": round(qbytes / (qms * 1e-3) / 1e9 / HBM_GBS, 4)}
+        extras["fp8_e4m3"] = fp8
+        del o8, codes
     result["extras"] = extras
 
     if not args.no_cpu_baseline:

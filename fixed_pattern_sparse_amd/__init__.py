@@ -243,10 +243,23 @@ def attention(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, descale_q
     return out
 
 
-def quantize_fp8(x, fp8_max: float = 448.0, eps: float = 1e-12):
-    """Per-tensor e4m3 quantization: returns (codes uint8, scale pair fp32[2])."""
+def quantize_fp8(x, fp8_max: float = 448.0, eps: float = 1e-12, scale_out=None):
+    """Per-tensor e4m3 quantization: returns (codes uint8, scale pair fp32[2]).
+    ``scale_out`` (2 fp32 on the device) receives {scale, 1/scale} if given."""
     import torch
     y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    sc = torch.empty(2, dtype=torch.float32, device=x.device)
+    sc = torch.empty(2, dtype=torch.float32, device=x.device) if scale_out is None else scale_out
     skiparse_quant_fp8(x.contiguous(), y, sc, fp8_max, eps)
     return y, sc
+
+
+def attention_fp8(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, fp8_max: float = 448.0,
+                  eps: float = 1e-12):
+    """The fp8 path end to end: quantize Q, K, V per tensor on the device, then
+    run the e4m3 attention kernel.  Returns (out bf16, codes (q, k, v),
+    scales fp32 (3, 2) = {scale, 1/scale} per tensor)."""
+    import torch
+    scales = torch.empty((3, 2), dtype=torch.float32, device=q.device)
+    codes = [quantize_fp8(t, fp8_max, eps, scale_out=scales[i])[0] for i, t in enumerate((q, k, v))]
+    out = attention(codes[0], codes[1], codes[2], kf, mode, softmax_scale, descale_qkv=scales)
+    return out, codes, scales

@@ -25,7 +25,9 @@
 //                  result exact (O and l share the same offset);
 //   O^T += V^T P^T  V^T comes from row-major V in LDS through
 //                  ds_read_b64_tr_b16; P^T stays in registers as bf16.
-#include "internal.h"
+#include <type_traits>
+
+#include "attn_common.h"
 
 namespace skiparse {
 namespace {
@@ -42,22 +44,10 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;   // queries per work-group
 constexpr float kTau = 8.0f;       // slack of the running max, log2 units
 constexpr int kTileBytes = kBN * 128 * 2;
-constexpr int kRowCap = 2048;      // capacity of the (t, h') row table
-constexpr int kColCap = 512;       // capacity of the w' column table
 
 __shared__ __attribute__((aligned(16))) char gKV[4 * kTileBytes];   // K0 K1 V0 V1
 __shared__ int32_t gRowBase[kRowCap];   // (t*H + h) * W for local row th = t*hr + h'
 __shared__ int32_t gColMap[kColCap];    // w for local column w'
-
-__device__ __forceinline__ int xcd_remap(int i, int n) {
-  // Work-groups are handed to the 8 XCDs round-robin.  Give each XCD one
-  // contiguous range of logical tiles, so the query tiles that stream the same
-  // subsequence's K/V run side by side on one XCD and share its L2.
-  constexpr int X = 8;
-  int xcd = i % X, local = i / X;
-  int per = n / X, rem = n % X;
-  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
-}
 
 template <int D>
 struct Layout {
@@ -90,19 +80,11 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   const int l32 = lane & 31;
 
   // ---- work item ---------------------------------------------------------
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = wg / a.tiles_per_bh;
-  const int rem = wg - bh * a.tiles_per_bh;
-  const int b = bh / a.heads;
-  const int head = bh - b * a.heads;
-  int si = 0;
-  while (si + 1 < a.n_run && a.sub[si + 1].tile0 <= rem) ++si;
-  const SubGeom sg = a.sub[si];
-  const int qtile = rem - sg.tile0;
+  const WorkItem wi = decode_work(a);
+  const SubGeom& sg = wi.sg;
+  const int b = wi.b, head = wi.head, qtile = wi.qtile;
   const int n = sg.n;
   const int nkv = (n + kBN - 1) / kBN;
-  const int wr = (int)sg.div_w.d;
-  const int th_end = n / wr;                 // T * hr
 
   const int64_t base = (int64_t)b * a.batch_stride + (int64_t)head * D;
   const __bf16* __restrict__ qp = (const __bf16*)a.q + base;
@@ -112,35 +94,13 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   const int64_t rs = a.row_stride;
   const uint32_t rsb = (uint32_t)a.row_stride * 2u;
 
-  // ---- row tables (FAST) ---------------------------------------------------
-  if constexpr (FAST) {
-    const int hr = th_end / a.g.T;
-    for (int x = tid; x < th_end; x += kThreads) {
-      const int t = x / hr;
-      const int hh = (int)axis_of_local((uint32_t)(x - t * hr), (uint32_t)sg.p, a.g);
-      gRowBase[x] = (t * a.g.H + hh) * a.g.W;
-    }
-    for (int x = tid; x < wr; x += kThreads) gColMap[x] = (int)axis_of_local((uint32_t)x, (uint32_t)sg.q, a.g);
-    __syncthreads();
-  }
-
   // ---- loader: thread owns chunk slot tid % CH of rows tid / CH + i*RSTEP ----
-  // For FAST each row walks through the tiles by its compact index
-  // j = tile*64 + r = th*wr + w', advanced by 64 = dth*wr + dw per tile.
+  if constexpr (FAST) build_row_tables(a, sg, gRowBase, gColMap, kThreads);
   const int lslot = tid % L::CH;
-  int st_th[L::CPT], st_w[L::CPT];
-  const int dth = kBN / wr, dw = kBN - (kBN / wr) * wr;
-  int tok_last = 0;
+  RowWalker<kBN> walk[L::CPT];
   if constexpr (FAST) {
 #pragma unroll
-    for (int i = 0; i < L::CPT; ++i) {
-      const int r = tid / L::CH + i * L::RSTEP;
-      st_th[i] = r / wr;
-      st_w[i] = r - st_th[i] * wr;
-    }
-    const int jl = n - 1;
-    const int tl = jl / wr;
-    tok_last = gRowBase[tl] + gColMap[jl - tl * wr];
+    for (int i = 0; i < L::CPT; ++i) walk[i].init(sg, tid / L::CH + i * L::RSTEP, gRowBase, gColMap);
   }
   struct Stage { uint4 k[L::CPT], v[L::CPT]; };   // staged chunks of a tile
   auto fetch = [&](int tile) -> Stage {
@@ -149,11 +109,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     for (int i = 0; i < L::CPT; ++i) {
       int tok;
       if constexpr (FAST) {
-        tok = st_th[i] < th_end ? gRowBase[st_th[i]] + gColMap[st_w[i]] : tok_last;
-        st_w[i] += dw;
-        const int cy = st_w[i] >= wr;
-        st_w[i] -= cy ? wr : 0;
-        st_th[i] += dth + cy;
+        tok = walk[i].next(gRowBase, gColMap);
         const uint32_t off = __umul24((uint32_t)tok, rsb) + (uint32_t)(lslot * 16);
         sgd.k[i] = *(const uint4*)(kb + off);
         sgd.v[i] = *(const uint4*)(vb + off);
@@ -196,13 +152,17 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
 
-  for (int j = 0; j < nkv; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < nkv;
+  // One tile.  BUF (the LDS buffer holding the tile) and LAST (the final tile:
+  // mask the keys past the end, nothing to prefetch) are compile-time, so the
+  // LDS addresses fold into immediates and the mask exists only in the last
+  // tile's copy.
+  auto tile = [&](int j, auto buf_tag, auto last_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr bool LAST = decltype(last_tag)::value;
     Stage nxt;
-    if (more) nxt = fetch(j + 1);   // in flight during this tile's compute
-    const char* sK = gKV + buf * kTileBytes;
-    const char* sV = gKV + (2 + buf) * kTileBytes;
+    if constexpr (!LAST) nxt = fetch(j + 1);   // in flight during this tile's compute
+    const char* sK = gKV + BUF * kTileBytes;
+    const char* sV = gKV + (2 + BUF) * kTileBytes;
 
     // S^T = K Q^T
     floatx16 s[2] = {floatx16{}, floatx16{}};
@@ -218,7 +178,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     }
 
     // online softmax
-    if ((j + 1) * kBN > n) {   // keys past the end of the subsequence
+    if constexpr (LAST) {   // keys past the end of the subsequence
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -290,8 +250,26 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
       }
     }
 
-    if (more) stash(nxt, buf ^ 1);   // the other buffer was last read before the previous barrier
-    __syncthreads();
+    if constexpr (!LAST) {
+      stash(nxt, BUF ^ 1);   // the other buffer was last read before the previous barrier
+      __syncthreads();
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using NotLast = std::integral_constant<bool, false>;
+  using Last = std::integral_constant<bool, true>;
+  int j = 0;
+  for (; j + 2 < nkv; j += 2) {
+    tile(j, I0{}, NotLast{});
+    tile(j + 1, I1{}, NotLast{});
+  }
+  if (j + 1 < nkv) {
+    tile(j, I0{}, NotLast{});
+    tile(j + 1, I1{}, Last{});
+  } else {
+    tile(j, I0{}, Last{});
   }
 
   // ---- normalize and scatter back to the original token rows ---------------
@@ -314,17 +292,7 @@ template <int D>
 hipError_t launch_d(AttnArgs a, int B, hipStream_t stream) {
   assign_tiles(a, B, kBM);
   if (a.total_tiles == 0) return hipSuccess;
-  // the fast path needs 24-bit tokens and row strides, 32-bit offsets per
-  // batch sample, and room for the row tables of every run subsequence
-  const int64_t tokens = (int64_t)a.g.T * a.g.H * a.g.W;
-  const int64_t rsb = (int64_t)a.row_stride * 2;
-  bool fast = tokens < (1 << 24) && rsb < (1 << 24) && tokens * rsb < (int64_t(1) << 32);
-  for (int i = 0; i < a.n_run && fast; ++i) {
-    const SubGeom& s = a.sub[i];
-    if (s.n == 0) continue;
-    const int64_t th = s.n / (int64_t)s.div_w.d;
-    fast = th <= kRowCap && (int64_t)s.div_w.d <= kColCap;
-  }
+  const bool fast = fast_rows_ok(a, (int64_t)a.row_stride * 2);
   if (fast)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
   else

@@ -16,7 +16,7 @@ struct AttnArgs {
   const void* k;
   const void* v;
   void* o;
-  const float* descale;     // FP8 only: {1/s_q, 1/s_k, 1/s_v} on the device
+  const float* descale;     // FP8 only: {s_q, 1/s_q, s_k, 1/s_k, s_v, 1/s_v} on the device
   int64_t batch_stride;     // elements per batch sample: T*H*W*heads*d
   int32_t row_stride;       // elements per token: heads*d
   int32_t heads;

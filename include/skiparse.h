@@ -134,9 +134,10 @@ int skiparse_index_map_device(const skiparse_plan* plan, int32_t* dev_gather, hi
  *                     SKIPARSE_FP8_E4M3: q/k/v e4m3 bytes quantized per
  *                     tensor (skiparse_quant_fp8), o bf16.
  *   softmax_scale     <= 0 selects 1/sqrt(d)
- *   dev_descale_qkv   FP8 only: device array of 3 fp32 {1/s_q, 1/s_k, 1/s_v}
- *                     (the second element of each skiparse_quant_fp8 scale
- *                     pair); NULL otherwise.  Q, K, V stand for code/s.
+ *   dev_descale_qkv   FP8 only: device array of 6 fp32
+ *                     {s_q, 1/s_q, s_k, 1/s_k, s_v, 1/s_v}, i.e. the three
+ *                     scale pairs skiparse_quant_fp8 writes, back to back;
+ *                     NULL otherwise.  Q, K, V stand for code / s.
  *   o                 must not overlap q, k or v.
  * Supported: d in {64, 128} (F32 and BF16), d == 128 (FP8); 1 <= k <= 8.
  * Errors: SKIPARSE_EINVAL, SKIPARSE_EUNSUPPORTED, SKIPARSE_EHIP.
