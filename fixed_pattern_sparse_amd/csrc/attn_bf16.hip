@@ -19,10 +19,13 @@
 //   S^T = K Q^T    v_mfma_f32_32x32x16_bf16; the transposed orientation
 //                  leaves one query per lane, so row statistics need one
 //                  cross-half swap and no shuffles;
-//   online softmax in the log2 domain with a lazily raised running max: the
-//                  accumulator is rescaled only when a tile's max exceeds the
-//                  running max by more than 2^8, which keeps p <= 256 and the
-//                  result exact (O and l share the same offset);
+//   online softmax in the log2 domain against a lazily raised running max:
+//                  p = exp2(s c - m) is formed with m as it stands, and only
+//                  when a lane's partial sum of p exceeds 2^20 (or is not
+//                  finite, as on the first tile) is the tile's max taken, O
+//                  and l rescaled and p formed again.  O and l always share
+//                  one offset, so the normalized result is exact, and every
+//                  p stays below 2^20, far inside fp32 and bf16 range;
 //   O^T += V^T P^T  V^T comes from row-major V in LDS through
 //                  ds_read_b64_tr_b16; P^T stays in registers as bf16.
 #include <type_traits>
@@ -42,7 +45,7 @@ constexpr int kBN = 64;            // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;   // queries per work-group
-constexpr float kTau = 8.0f;       // slack of the running max, log2 units
+constexpr float kBig = 1048576.0f; // 2^20: bound on a lane's partial sum before the max is raised
 constexpr int kTileBytes = kBN * 128 * 2;
 
 __shared__ __attribute__((aligned(16))) char gKV[4 * kTileBytes];   // K0 K1 V0 V1
@@ -141,7 +144,12 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   const bool qok = jq < n;
   const int64_t qoff = (int64_t)token_of((uint32_t)(qok ? jq : n - 1), sg, a.g) * rs;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const bf16x8*)(qp + qoff + kk * 16 + hl * 8);
+  for (int kk = 0; kk < KK; ++kk) {
+    qf[kk] = *(const bf16x8*)(qp + qoff + kk * 16 + hl * 8);
+    // pin the fragment in registers: otherwise the compiler re-loads Q from
+    // global memory inside the key loop and every QK MFMA waits on it
+    __asm__ volatile("" : "+v"(qf[kk]));
+  }
 
   stash(first, 0);
   __syncthreads();
@@ -164,16 +172,30 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     const char* sK = gKV + BUF * kTileBytes;
     const char* sV = gKV + (2 + BUF) * kTileBytes;
 
-    // S^T = K Q^T
+    // S^T = K Q^T; the K fragments of step kk+1 are read while step kk's
+    // MFMAs run, so LDS latency hides behind the matrix core
+    auto kfrag = [&](int kk, int mb) -> bf16x8 {
+      const int row = mb * 32 + l32;
+      const int ch = (2 * kk + hl) ^ L::kswz(row);
+      return *(const bf16x8*)(sK + row * L::ROWB + ch * 16);
+    };
     floatx16 s[2] = {floatx16{}, floatx16{}};
+    bf16x8 kcur[2] = {kfrag(0, 0), kfrag(0, 1)};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
+      bf16x8 knext[2];
+      if (kk + 1 < KK) {
+        knext[0] = kfrag(kk + 1, 0);
+        knext[1] = kfrag(kk + 1, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int row = mb * 32 + l32;
-        const int ch = (2 * kk + hl) ^ L::kswz(row);
-        const bf16x8 kf = *(const bf16x8*)(sK + row * L::ROWB + ch * 16);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[mb], 0, 0, 0);
+      for (int mb = 0; mb < 2; ++mb)
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[mb], qf[kk], s[mb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < KK) {
+        kcur[0] = knext[0];
+        kcur[1] = knext[1];
       }
     }
 
@@ -187,19 +209,39 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
           if (key >= n) s[mb][i] = -INFINITY;
         }
     }
-    float mx = s[0][0];
+    // P = exp2(S c - m) with the running max as it stands; the tile's own
+    // max is taken only when some p could exceed kBig (the partial sum of a
+    // lane bounds each of its terms), which also covers the first tile
+    bf16x8 pk[2][2];
+    float lsum;
+    auto exps = [&]() {
+      const float mneg = -m_run;
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    {
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][cc * 8 + 2 * e], c, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][cc * 8 + 2 * e + 1], c, mneg));
+            ls[mb * 2 + cc] += p0 + p1;
+            pk[mb][cc][2 * e] = (__bf16)p0;
+            pk[mb][cc][2 * e + 1] = (__bf16)p1;
+          }
+      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    exps();
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= kBig))) {
+      // rare: raise the running max, rescale, and redo the tile
+      float mx = s[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mx2 = mx * c;
-    if (__builtin_amdgcn_ballot_w64(mx2 > m_run + kTau)) {
-      // rare: raise the running max and rescale
-      const float mnew = fmaxf(m_run, mx2);
+      const float mnew = fmaxf(m_run, mx * c);
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
       m_run = mnew;
       l_run *= alpha;
@@ -209,45 +251,37 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] = __builtin_fmaf(acc[db][i], alpha, 0.0f);
+      exps();
     }
-    const float mneg = -m_run;
-    bf16x8 pk[2][2];
-    float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][cc * 8 + 2 * e], c, mneg));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][cc * 8 + 2 * e + 1], c, mneg));
-          lsum[mb * 2 + cc] += p0 + p1;
-          pk[mb][cc][2 * e] = (__bf16)p0;
-          pk[mb][cc][2 * e + 1] = (__bf16)p1;
-        }
-    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    l_run += lsum;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; V fragments are read one step ahead of their MFMA
+    auto vfrag = [&](int step) -> bf16x8 {   // step = (db * 2 + mb) * 2 + cc
+      const int db = step >> 2, mb = (step >> 1) & 1, cc = step & 1;
+      shortx4 part[2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          shortx4 part[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const int row = mb * 32 + cc * 16 + x * 8 + hl * 4 + ((lane & 15) >> 2);
-            const int col = db * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;   // elements
-            const int ch = (col >> 3) ^ L::vswz(row);
-            part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_shortx4*)(sV + row * L::ROWB + ch * 16 + (col & 7) * 2));
-          }
-          bf16x8 vf;
-          __builtin_memcpy(&vf, part, 16);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[mb][cc], acc[db], 0, 0, 0);
-        }
+      for (int x = 0; x < 2; ++x) {
+        const int row = mb * 32 + cc * 16 + x * 8 + hl * 4 + ((lane & 15) >> 2);
+        const int col = db * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;   // elements
+        const int ch = (col >> 3) ^ L::vswz(row);
+        part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_shortx4*)(sV + row * L::ROWB + ch * 16 + (col & 7) * 2));
       }
+      bf16x8 vf;
+      __builtin_memcpy(&vf, part, 16);
+      return vf;
+    };
+    constexpr int PVS = DB * 4;
+    bf16x8 vcur = vfrag(0);
+#pragma unroll
+    for (int step = 0; step < PVS; ++step) {
+      bf16x8 vnext;
+      if (step + 1 < PVS) vnext = vfrag(step + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int db = step >> 2, mb = (step >> 1) & 1, cc = step & 1;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pk[mb][cc], acc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (step + 1 < PVS) vcur = vnext;
     }
 
     if constexpr (!LAST) {

@@ -110,6 +110,31 @@ def test_bf16_small_full_compare(shp, kf, mode):
     assert err_ratio(to_np64(o), r) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_running_max_moves(direction, dtype):
+    """Key norms ramp along the token order, so the row max moves across key
+    tiles.  Rising: the max has to be raised on most tiles; falling: only on
+    the first.  Several 64-key tiles and a ragged tail per subsequence.
+    bf16 ramps to 40x: scores reach ~190 in log2 units, so an exp2 taken
+    against a stale max would overflow fp32.  f32 ramps to 8x: at 40x, fp32
+    rounding of the 128-term dot products alone moves the output by ~1.7e-5
+    (plain float32 numpy attention does the same), beyond the 1e-5 bar that
+    holds for N(0,1) inputs."""
+    shp = (1, 3, 16, 42, 2, 128)
+    kf, mode = 2, 0
+    q, k, v = (wl.normal_tensor(shp, 17, i) for i in range(3))
+    N = shp[1] * shp[2] * shp[3]
+    top = 40.0 if dtype == "bf16" else 8.0
+    ramp = np.linspace(1.0, top, N) if direction == "rising" else np.linspace(top, 1.0, N)
+    k = k * ramp.reshape(1, shp[1], shp[2], shp[3], 1, 1)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(tdt) for x in (q, k, v))
+    o = run(q, k, v, kf, mode)
+    r = ref.skiparse_attention(to_np64(q), to_np64(k), to_np64(v), kf, mode)
+    assert err_ratio(to_np64(o), r) <= TOL[dtype]
+
+
 def test_bf16_writes_exactly_the_real_rows_of_run_subsequences():
     """NaN-prefilled output: a call over subsequences [1, 3) writes every row of
     those subsequences and no other row."""
