@@ -51,6 +51,8 @@ constexpr int kTileBytes = kBN * 128 * 2;
 __shared__ __attribute__((aligned(16))) char gKV[4 * kTileBytes];   // K0 K1 V0 V1
 __shared__ int32_t gRowBase[kRowCap];   // (t*H + h) * W for local row th = t*hr + h'
 __shared__ int32_t gColMap[kColCap];    // w for local column w'
+constexpr int kTokCap = 24064;          // token table: the whole subsequence
+__shared__ int32_t gTok[kTokCap];       // token of compact member j
 
 template <int D>
 struct Layout {
@@ -65,10 +67,12 @@ struct Layout {
   __device__ static int vswz(int r) { return D == 128 ? ((r & 3) << 2) : ((r & 1) << 2); }
 };
 
-// FAST: token rows come from the LDS tables, offsets are 32-bit from a scalar
-// base (needs T*H*W < 2^24, heads*d*2 < 2^24, a batch sample's tensor < 4 GB
-// and table room).  Otherwise the index function is evaluated per row.
-template <int D, bool FAST>
+// ROWS selects where a key row's token comes from.  2: a table of the whole
+// subsequence's tokens, written once per work-group (n <= kTokCap); 1: a
+// walker over the (t, h') row and w' column tables (table room needed); both
+// use 32-bit offsets from a scalar base (T*H*W < 2^24, heads*d*2 < 2^24, a
+// batch sample's tensor < 4 GB).  0: the index function per row.
+template <int D, int ROWS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const AttnArgs a) {
   using L = Layout<D>;
@@ -98,10 +102,15 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   const uint32_t rsb = (uint32_t)a.row_stride * 2u;
 
   // ---- loader: thread owns chunk slot tid % CH of rows tid / CH + i*RSTEP ----
-  if constexpr (FAST) build_row_tables(a, sg, gRowBase, gColMap, kThreads);
+  if constexpr (ROWS == 2) {
+    for (int x = tid; x < n; x += kThreads) gTok[x] = (int)token_of((uint32_t)x, sg, a.g);
+    __syncthreads();
+  } else if constexpr (ROWS == 1) {
+    build_row_tables(a, sg, gRowBase, gColMap, kThreads);
+  }
   const int lslot = tid % L::CH;
   RowWalker<kBN> walk[L::CPT];
-  if constexpr (FAST) {
+  if constexpr (ROWS == 1) {
 #pragma unroll
     for (int i = 0; i < L::CPT; ++i) walk[i].init(sg, tid / L::CH + i * L::RSTEP, gRowBase, gColMap);
   }
@@ -111,7 +120,14 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < L::CPT; ++i) {
       int tok;
-      if constexpr (FAST) {
+      if constexpr (ROWS == 2) {
+        int jr = tile * kBN + tid / L::CH + i * L::RSTEP;
+        jr = jr < n ? jr : n - 1;
+        tok = gTok[jr];
+        const uint32_t off = __umul24((uint32_t)tok, rsb) + (uint32_t)(lslot * 16);
+        sgd.k[i] = *(const uint4*)(kb + off);
+        sgd.v[i] = *(const uint4*)(vb + off);
+      } else if constexpr (ROWS == 1) {
         tok = walk[i].next(gRowBase, gColMap);
         const uint32_t off = __umul24((uint32_t)tok, rsb) + (uint32_t)(lslot * 16);
         sgd.k[i] = *(const uint4*)(kb + off);
@@ -326,11 +342,13 @@ template <int D>
 hipError_t launch_d(AttnArgs a, int B, hipStream_t stream) {
   assign_tiles(a, B, kBM);
   if (a.total_tiles == 0) return hipSuccess;
-  const bool fast = fast_rows_ok(a, (int64_t)a.row_stride * 2);
-  if (fast)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+  const int64_t row_bytes = (int64_t)a.row_stride * 2;
+  if (token_table_ok(a, row_bytes, kTokCap))
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+  else if (fast_rows_ok(a, row_bytes))
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 0>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -87,11 +87,25 @@ struct RowWalker {
   }
 };
 
-// Whether every run subsequence fits the tables and 32-bit offsets work:
-// 24-bit tokens and row strides, and a batch sample's tensor below 4 GB.
-inline bool fast_rows_ok(const AttnArgs& a, int64_t row_bytes) {
+// Whether 32-bit row offsets work: 24-bit tokens and row strides, and a
+// batch sample's tensor below 4 GB.
+inline bool offsets32_ok(const AttnArgs& a, int64_t row_bytes) {
   const int64_t tokens = (int64_t)a.g.T * a.g.H * a.g.W;
-  bool fast = tokens < (1 << 24) && row_bytes < (1 << 24) && tokens * row_bytes < (int64_t(1) << 32);
+  return tokens < (1 << 24) && row_bytes < (1 << 24) && tokens * row_bytes < (int64_t(1) << 32);
+}
+
+// Whether every run subsequence holds at most cap members (its whole token
+// list then fits one LDS table) and 32-bit offsets work.
+inline bool token_table_ok(const AttnArgs& a, int64_t row_bytes, int cap) {
+  bool ok = offsets32_ok(a, row_bytes);
+  for (int i = 0; i < a.n_run && ok; ++i) ok = a.sub[i].n <= cap;
+  return ok;
+}
+
+// Whether every run subsequence fits the row/column tables and 32-bit
+// offsets work.
+inline bool fast_rows_ok(const AttnArgs& a, int64_t row_bytes) {
+  bool fast = offsets32_ok(a, row_bytes);
   for (int i = 0; i < a.n_run && fast; ++i) {
     const SubGeom& s = a.sub[i];
     if (s.n == 0) continue;

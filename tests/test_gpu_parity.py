@@ -7,6 +7,8 @@ tails; the full workload shapes are compared on sampled rows (first/last rows,
 the padding edge, every subsequence) that the oracle computes one by one.
 """
 
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -226,6 +228,19 @@ def test_bf16_workload_sampled(name, kf, mode):
     torch.cuda.synchronize()
     heads = [0, w.heads // 2, w.heads - 1]
     check_sampled(w, cpu, out, kf, mode, heads, seed=kf * 10 + mode, tol=TOL["bf16"])
+
+
+@pytest.mark.parametrize("shp,kf,mode", [
+    ((1, 1, 24, 1100, 1, 64), 1, 0),   # n = 26400 over the token-table cap, 1100 columns: index function per row
+    ((1, 2, 60, 220, 1, 64), 1, 0),    # n = 26400 over the cap, row/column tables fit: table walker
+    ((1, 1, 8, 2200, 1, 64), 2, 1),    # n = 4400 with 1100 local columns: token table
+])
+def test_bf16_row_sources(shp, kf, mode):
+    """The kernel finds a key row's token in one of three ways, chosen by the
+    subsequence sizes; each is checked on sampled rows."""
+    q, k, v = (torch.from_numpy(wl.normal_tensor(shp, 23, i)).to(torch.bfloat16) for i in range(3))
+    out = run(q, k, v, kf, mode)
+    check_sampled(types.SimpleNamespace(shape=shp), (q, k, v), out, kf, mode, [0], seed=3, tol=TOL["bf16"])
 
 
 # ---------------------------------------------------------------------------
