@@ -31,8 +31,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HBM_GBS = 8000.0
 COPY_BYTES = 1 << 30          # calibration copy of the traffic run
 PROFILE_PMC = os.path.join(ROOT, "profiles", "attn_fwd_bf16_720p_5s_pmc.md")
-KERNEL_SOURCES = ["fixed_pattern_sparse_amd/csrc/attn_bf16.hip", "fixed_pattern_sparse_amd/csrc/geom.h",
-                  "fixed_pattern_sparse_amd/csrc/internal.h"]
+KERNEL_SOURCES = ["fixed_pattern_sparse_amd/csrc/attn_bf16.hip", "fixed_pattern_sparse_amd/csrc/attn_common.h",
+                  "fixed_pattern_sparse_amd/csrc/geom.h", "fixed_pattern_sparse_amd/csrc/internal.h"]
 
 
 def kernel_source_hash() -> str:
@@ -192,7 +192,7 @@ def main():
                    "step": "token-wise layer + group-wise layer", "flop_per_step": flops_step},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128, true>",
+                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128, 2>",
                      "avg_launch_ms": round(avg_launch_ms, 4)},
     }
     extras = {"ms_per_layer": round(ms_step / 2, 4)}
