@@ -22,6 +22,10 @@ Modules:
   pad/reshape/transpose, masked attention per subsequence (float64), brute
   force block-masked full attention, and sampled-row evaluation for full-size
   shapes.
+* :mod:`oracle.skiparse_bwd` -- the gradients dQ, dK, dV of the same attention
+  for an upstream dO (the chain rule through softmax attention, per
+  subsequence), the per-query log-sum-exp, and sampled-row evaluators for
+  full-size shapes.
 * :mod:`oracle.fp8_ref` -- OCP FP8 E4M3 codec from the format definition and the
   per-tensor amax scale rule.
 * :mod:`oracle.cpu_baseline` -- the same algorithm in fp32 numpy/BLAS, timed
@@ -29,6 +33,7 @@ Modules:
 
 Every function is pinned by ``-m "not gpu"`` tests against values the pages
 and the mathematics fix (hand-derived golden maps, torch's pixel_unshuffle,
-textbook softmax attention, closed forms, invariants).  No function here is
+textbook softmax attention, closed forms, invariants; for the gradients:
+finite differences of the forward oracle and torch's float64 autograd).  No function here is
 "parity unpinned".
 """
