@@ -10,13 +10,21 @@ The names mirror the C ABI in include/skiparse.h:
     skiparse_index_map_device(plan, out, stream=None)
     skiparse_attn_fwd(plan, dtype, q, k, v, o, softmax_scale=0.0,
                       descale_qkv=None, sub_begin=0, sub_count=0, stream=None)
+    skiparse_attn_fwd_lse(plan, dtype, q, k, v, o, lse, softmax_scale=0.0,
+                          sub_begin=0, sub_count=0, stream=None)
+    skiparse_attn_bwd_workspace_bytes(plan)
+    skiparse_attn_bwd(plan, dtype, q, k, v, o, dout, lse, dq, dk, dv,
+                      softmax_scale=0.0, workspace=None, sub_begin=0,
+                      sub_count=0, stream=None)
     skiparse_quant_fp8_workspace_bytes(numel)
     skiparse_quant_fp8(x, y, scale, fp8_max=448.0, eps=1e-12,
                        workspace=None, stream=None)
     skiparse_last_error()
 
-plus two conveniences that allocate their outputs with torch:
-``attention(q, k, v, kf, mode)`` and ``quantize_fp8(x)``.
+plus conveniences that allocate their outputs with torch:
+``attention``, ``attention_fp8``, ``quantize_fp8``, ``attention_train``
+(output and log-sum-exp), ``attention_bwd`` (dq, dk, dv) and
+``SkiparseAttention`` (a torch.autograd.Function over the last two).
 
 There is no fallback: if libskiparse.so is missing the calls raise.
 """
@@ -53,6 +61,9 @@ EXPORTED = (
     "skiparse_plan_index_map",
     "skiparse_index_map_device",
     "skiparse_attn_fwd",
+    "skiparse_attn_fwd_lse",
+    "skiparse_attn_bwd_workspace_bytes",
+    "skiparse_attn_bwd",
     "skiparse_quant_fp8_workspace_bytes",
     "skiparse_quant_fp8",
     "skiparse_last_error",
@@ -114,6 +125,14 @@ def lib():
     L.skiparse_attn_fwd.restype = ctypes.c_int
     L.skiparse_attn_fwd.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, ctypes.c_float, vp,
                                     ctypes.c_int32, ctypes.c_int32, vp]
+    L.skiparse_attn_fwd_lse.restype = ctypes.c_int
+    L.skiparse_attn_fwd_lse.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_float,
+                                        ctypes.c_int32, ctypes.c_int32, vp]
+    L.skiparse_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.skiparse_attn_bwd_workspace_bytes.argtypes = [P]
+    L.skiparse_attn_bwd.restype = ctypes.c_int
+    L.skiparse_attn_bwd.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                    vp, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, vp]
     L.skiparse_quant_fp8_workspace_bytes.restype = ctypes.c_size_t
     L.skiparse_quant_fp8_workspace_bytes.argtypes = [ctypes.c_int64]
     L.skiparse_quant_fp8.restype = ctypes.c_int
@@ -185,6 +204,32 @@ def skiparse_attn_fwd(plan: SkiparsePlan, dtype: int, q, k, v, o, softmax_scale:
                                    float(softmax_scale), _ptr(descale_qkv), sub_begin, sub_count,
                                    _stream(stream)))
     return o
+
+
+def skiparse_attn_fwd_lse(plan: SkiparsePlan, dtype: int, q, k, v, o, lse, softmax_scale: float = 0.0,
+                          sub_begin: int = 0, sub_count: int = 0, stream=None):
+    _check(lib().skiparse_attn_fwd_lse(ctypes.byref(plan), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       float(softmax_scale), sub_begin, sub_count, _stream(stream)))
+    return o, lse
+
+
+def skiparse_attn_bwd_workspace_bytes(plan: SkiparsePlan) -> int:
+    return int(lib().skiparse_attn_bwd_workspace_bytes(ctypes.byref(plan)))
+
+
+def skiparse_attn_bwd(plan: SkiparsePlan, dtype: int, q, k, v, o, dout, lse, dq, dk, dv,
+                      softmax_scale: float = 0.0, workspace=None, sub_begin: int = 0, sub_count: int = 0,
+                      stream=None):
+    """Backward pass; ``workspace`` (device, >= skiparse_attn_bwd_workspace_bytes)
+    is allocated with torch when None."""
+    if workspace is None:
+        import torch
+        workspace = torch.empty(skiparse_attn_bwd_workspace_bytes(plan), dtype=torch.uint8, device=q.device)
+    wb = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    _check(lib().skiparse_attn_bwd(ctypes.byref(plan), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                   _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), float(softmax_scale), _ptr(workspace),
+                                   wb, sub_begin, sub_count, _stream(stream)))
+    return dq, dk, dv
 
 
 def skiparse_quant_fp8_workspace_bytes(numel: int) -> int:
@@ -263,3 +308,63 @@ def attention_fp8(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, fp8_m
     codes = [quantize_fp8(t, fp8_max, eps, scale_out=scales[i])[0] for i, t in enumerate((q, k, v))]
     out = attention(codes[0], codes[1], codes[2], kf, mode, softmax_scale, descale_qkv=scales)
     return out, codes, scales
+
+
+def attention_train(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, plan: SkiparsePlan | None = None):
+    """Training forward on bf16 (B, T, H, W, heads, d) device tensors: returns
+    (out, lse) with lse fp32 (B, T*H*W, heads)."""
+    import torch
+    if q.dim() != 6 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one (B, T, H, W, heads, d) shape")
+    B, T, H, W, nh, d = q.shape
+    if plan is None:
+        plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, T * H * W, nh), dtype=torch.float32, device=q.device)
+    skiparse_attn_fwd_lse(plan, _dtype_code(q), q.contiguous(), k.contiguous(), v.contiguous(), out, lse,
+                          softmax_scale)
+    return out, lse
+
+
+def attention_bwd(q, k, v, o, dout, lse, kf: int, mode: int, softmax_scale: float = 0.0,
+                  plan: SkiparsePlan | None = None):
+    """Backward pass on bf16 device tensors: returns (dq, dk, dv)."""
+    import torch
+    B, T, H, W, nh, d = q.shape
+    if plan is None:
+        plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    skiparse_attn_bwd(plan, _dtype_code(q), q.contiguous(), k.contiguous(), v.contiguous(), o.contiguous(),
+                      dout.contiguous(), lse, dq, dk, dv, softmax_scale)
+    return dq, dk, dv
+
+
+def _autograd_function():
+    import torch
+
+    class SkiparseAttention(torch.autograd.Function):
+        """Skiparse-2D attention as a torch autograd op (bf16, device):
+        ``SkiparseAttention.apply(q, k, v, kf, mode)``."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, kf, mode):
+            out, lse = attention_train(q, k, v, kf, mode)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.kf, ctx.mode = kf, mode
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse = ctx.saved_tensors
+            dq, dk, dv = attention_bwd(q, k, v, out, dout, lse, ctx.kf, ctx.mode)
+            return dq, dk, dv, None, None
+
+    return SkiparseAttention
+
+
+def __getattr__(name):
+    if name == "SkiparseAttention":
+        cls = _autograd_function()
+        globals()[name] = cls
+        return cls
+    raise AttributeError(name)

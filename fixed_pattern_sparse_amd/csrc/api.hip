@@ -247,6 +247,121 @@ int skiparse_attn_fwd(const skiparse_plan* plan, skiparse_dtype dtype, const voi
   return ok();
 }
 
+namespace {
+
+// Range, scale and common-pointer checks shared by the training entry points;
+// fills the call-wide part of AttnArgs.
+int training_args(const skiparse_plan* plan, skiparse_dtype dtype, float softmax_scale, int32_t sub_begin,
+                  int32_t& sub_count, AttnArgs& a) {
+  if (dtype != SKIPARSE_BF16) return fail(SKIPARSE_EUNSUPPORTED, "training calls are built for BF16 only");
+  if (sub_count == 0) {
+    if (sub_begin != 0) return fail(SKIPARSE_EINVAL, "sub_count == 0 (all) needs sub_begin == 0");
+    sub_count = plan->n_sub;
+  }
+  if (sub_begin < 0 || sub_count < 0 || sub_begin + sub_count > plan->n_sub)
+    return fail(SKIPARSE_EINVAL, "subsequence range [%d, %d) outside [0, %d)", sub_begin, sub_begin + sub_count, plan->n_sub);
+  if (!(std::isfinite(softmax_scale))) return fail(SKIPARSE_EINVAL, "softmax_scale must be finite");
+  const int d = plan->d;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
+  std::memset(&a, 0, sizeof a);
+  a.batch_stride = (int64_t)plan->T * plan->H * plan->W * plan->heads * d;
+  a.row_stride = plan->heads * d;
+  a.heads = plan->heads;
+  a.n_run = sub_count;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  make_geom(*plan, a.g);
+  for (int i = 0; i < sub_count; ++i) a.sub[i] = make_sub(*plan, sub_begin + i);
+  return SKIPARSE_OK;
+}
+
+int64_t row_count(const skiparse_plan* plan) { return (int64_t)plan->B * plan->T * plan->H * plan->W * plan->heads; }
+
+}  // namespace
+
+int skiparse_attn_fwd_lse(const skiparse_plan* plan, skiparse_dtype dtype, const void* q, const void* k,
+                          const void* v, void* o, float* lse, float softmax_scale, int32_t sub_begin,
+                          int32_t sub_count, hipStream_t stream) {
+  if (int e = check_plan(plan)) return e;
+  AttnArgs a;
+  if (int e = training_args(plan, dtype, softmax_scale, sub_begin, sub_count, a)) return e;
+  const int d = plan->d;
+  if (d != 64 && d != 128) return fail(SKIPARSE_EUNSUPPORTED, "d=%d is not built (64 or 128)", d);
+  if (!q || !k || !v || !o || !lse) return fail(SKIPARSE_EINVAL, "q, k, v, o and lse must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SKIPARSE_EINVAL, "q, k, v and o must be 16-byte aligned");
+  if (((uintptr_t)lse & 3u) != 0) return fail(SKIPARSE_EINVAL, "lse must be 4-byte aligned");
+  const int64_t bytes = row_count(plan) * d * 2;
+  const int64_t lbytes = row_count(plan) * 4;
+  if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
+    return fail(SKIPARSE_EINVAL, "o must not overlap q, k or v");
+  if (overlap(lse, lbytes, q, bytes) || overlap(lse, lbytes, k, bytes) || overlap(lse, lbytes, v, bytes) ||
+      overlap(lse, lbytes, o, bytes))
+    return fail(SKIPARSE_EINVAL, "lse must not overlap q, k, v or o");
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  (void)hipGetLastError();
+  const hipError_t e = launch_attn_bf16(a, plan->B, d, stream);
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t skiparse_attn_bwd_workspace_bytes(const skiparse_plan* plan) {
+  if (check_plan(plan)) return 0;
+  return (size_t)row_count(plan) * sizeof(float);
+}
+
+int skiparse_attn_bwd(const skiparse_plan* plan, skiparse_dtype dtype, const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float softmax_scale, void* workspace, size_t workspace_bytes, int32_t sub_begin,
+                      int32_t sub_count, hipStream_t stream) {
+  if (int e = check_plan(plan)) return e;
+  AttnArgs a;
+  if (int e = training_args(plan, dtype, softmax_scale, sub_begin, sub_count, a)) return e;
+  const int d = plan->d;
+  if (d != 128) return fail(SKIPARSE_EUNSUPPORTED, "the backward pass is built for d=128 only (d=%d)", d);
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(SKIPARSE_EINVAL, "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL");
+  for (const void* x : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(x)) return fail(SKIPARSE_EINVAL, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  if (((uintptr_t)lse & 3u) != 0) return fail(SKIPARSE_EINVAL, "lse must be 4-byte aligned");
+  const size_t need = skiparse_attn_bwd_workspace_bytes(plan);
+  if (!workspace || workspace_bytes < need)
+    return fail(SKIPARSE_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace & 3u) != 0) return fail(SKIPARSE_EINVAL, "workspace must be 4-byte aligned");
+  const int64_t bytes = row_count(plan) * d * 2;
+  const int64_t lbytes = row_count(plan) * 4;
+  const void* ins[] = {q, k, v, o, dout};
+  const int64_t insz[] = {bytes, bytes, bytes, bytes, bytes};
+  void* outs[] = {dq, dk, dv, workspace};
+  const int64_t outsz[] = {bytes, bytes, bytes, (int64_t)need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return fail(SKIPARSE_EINVAL, "outputs and workspace must not overlap the inputs");
+    if (overlap(outs[i], outsz[i], lse, lbytes)) return fail(SKIPARSE_EINVAL, "outputs and workspace must not overlap lse");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(SKIPARSE_EINVAL, "dq, dk, dv and workspace must not overlap");
+  }
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = const_cast<void*>(o);   // read only by the backward kernels
+  a.dout = dout;
+  a.lse = const_cast<float*>(lse);
+  a.dsum = (float*)workspace;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  (void)hipGetLastError();
+  const hipError_t e = launch_attn_bwd(a, plan->B, d, stream);
+  if (e == hipErrorNotSupported) return fail(SKIPARSE_EUNSUPPORTED, "this head dim has no backward kernel in this build");
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t skiparse_quant_fp8_workspace_bytes(int64_t numel) { return quant_workspace_bytes(numel < 0 ? 0 : numel); }
 
 int skiparse_quant_fp8(const void* x, skiparse_dtype x_dtype, int64_t numel, uint8_t* y, float* dev_scale,

@@ -158,7 +158,8 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   bf16x8 qf[KK];
   const int jq = qtile * kBM + wave * 32 + l32;
   const bool qok = jq < n;
-  const int64_t qoff = (int64_t)token_of((uint32_t)(qok ? jq : n - 1), sg, a.g) * rs;
+  const int tokq = (int)token_of((uint32_t)(qok ? jq : n - 1), sg, a.g);
+  const int64_t qoff = (int64_t)tokq * rs;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     qf[kk] = *(const bf16x8*)(qp + qoff + kk * 16 + hl * 8);
@@ -324,7 +325,14 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
 
   // ---- normalize and scatter back to the original token rows ---------------
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-  const float inv = 1.0f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+  const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  const float inv = 1.0f / l_tot;
+  if (a.lse != nullptr && qok && hl == 0) {
+    // both lane halves hold the same running max; log of the denominator in
+    // natural units: ln 2 * (m + log2 l), m being in log2 units of s*scale
+    const int64_t N = (int64_t)a.g.T * a.g.H * a.g.W;
+    a.lse[((int64_t)b * N + tokq) * a.heads + head] = 0.69314718055994531f * (m_run + __log2f(l_tot));
+  }
   if (qok) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)

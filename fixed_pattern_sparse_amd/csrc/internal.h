@@ -17,6 +17,12 @@ struct AttnArgs {
   const void* v;
   void* o;
   const float* descale;     // FP8 only: {s_q, 1/s_q, s_k, 1/s_k, s_v, 1/s_v} on the device
+  float* lse;               // forward (bf16): natural-log softmax denominators, (B, T*H*W, heads), or NULL
+  const void* dout;         // backward: upstream gradient dO, same layout as o
+  float* dsum;              // backward: rowsum(dO * O), (B, T*H*W, heads), written by the first kernel
+  void* dq;                 // backward outputs, same layout as q
+  void* dk;
+  void* dv;
   int64_t batch_stride;     // elements per batch sample: T*H*W*heads*d
   int32_t row_stride;       // elements per token: heads*d
   int32_t heads;
@@ -45,6 +51,7 @@ inline void assign_tiles(AttnArgs& a, int B, int bm) {
 hipError_t launch_attn_bf16(AttnArgs a, int B, int d, hipStream_t stream);
 hipError_t launch_attn_f32(AttnArgs a, int B, int d, hipStream_t stream);
 hipError_t launch_attn_fp8(AttnArgs a, int B, int d, hipStream_t stream);
+hipError_t launch_attn_bwd(AttnArgs a, int B, int d, hipStream_t stream);
 hipError_t launch_index_map(const Geom& g, const SubGeom* subs, int n_sub, int sub_h, int sub_w,
                             int32_t* out, hipStream_t stream);
 size_t quant_workspace_bytes(int64_t numel);

@@ -147,6 +147,55 @@ int skiparse_attn_fwd(const skiparse_plan* plan, skiparse_dtype dtype,
                       float softmax_scale, const float* dev_descale_qkv,
                       int32_t sub_begin, int32_t sub_count, hipStream_t stream);
 
+/*
+ * Training forward: skiparse_attn_fwd for SKIPARSE_BF16 that also keeps, for
+ * every real query token x of the run subsequences, the natural-log softmax
+ * denominator the backward pass needs (the sparse model is fine-tuned and
+ * trained with this attention: OSP-Next summary, method steps and
+ * reproduction):
+ *     lse[(b * T*H*W + x) * heads + head] = log sum_y exp(softmax_scale * <Q[x], K[y]>)
+ * over the real tokens y of x's subsequence.  o as in skiparse_attn_fwd.
+ *   lse      device fp32, B * T*H*W * heads entries (layout (B, T*H*W, heads)),
+ *            4-byte aligned; entries of tokens outside the run subsequences
+ *            are not written.  Must not overlap q, k, v or o.
+ * Supported: SKIPARSE_BF16, d in {64, 128}.
+ * Errors: SKIPARSE_EINVAL, SKIPARSE_EUNSUPPORTED, SKIPARSE_EHIP.
+ */
+int skiparse_attn_fwd_lse(const skiparse_plan* plan, skiparse_dtype dtype,
+                          const void* q, const void* k, const void* v, void* o, float* lse,
+                          float softmax_scale, int32_t sub_begin, int32_t sub_count, hipStream_t stream);
+
+/* Workspace bytes skiparse_attn_bwd needs: B * T*H*W * heads * 4 (one fp32
+ * per row); 0 for an invalid plan. */
+size_t skiparse_attn_bwd_workspace_bytes(const skiparse_plan* plan);
+
+/*
+ * Backward pass: the gradients of skiparse_attn_fwd's output with respect to
+ * its inputs, for an upstream gradient dout of the same layout as o.  Inside
+ * each run subsequence s, with S = softmax_scale * Q K^T over its real tokens,
+ * P = softmax(S) by rows (from lse: P = exp(S - lse)), O = P V:
+ *     dV = P^T dO,   dS = P * (dO V^T - rowsum(dO * O)),
+ *     dQ = softmax_scale * dS K,   dK = softmax_scale * dS^T Q.
+ * Rows of dq, dk, dv of the run subsequences' real tokens are written; other
+ * rows are not.  Each subsequence is independent, so runs over disjoint
+ * subsequence ranges may go to one set of outputs.
+ *   q, k, v, o, dout   device bf16 (B, T, H, W, heads, d); o and lse as
+ *                      written by skiparse_attn_fwd_lse with the same scale
+ *   lse                device fp32 (B, T*H*W, heads), 4-byte aligned
+ *   dq, dk, dv         device bf16, same layout as q; must not overlap each
+ *                      other, the inputs or the workspace
+ *   workspace          device, at least skiparse_attn_bwd_workspace_bytes,
+ *                      4-byte aligned, caller-owned scratch (rowsum(dO * O))
+ * Supported: SKIPARSE_BF16, d == 128, 1 <= k <= 8.
+ * Errors: SKIPARSE_EINVAL, SKIPARSE_EUNSUPPORTED, SKIPARSE_EWORKSPACE,
+ * SKIPARSE_EHIP.
+ */
+int skiparse_attn_bwd(const skiparse_plan* plan, skiparse_dtype dtype,
+                      const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, float softmax_scale,
+                      void* workspace, size_t workspace_bytes,
+                      int32_t sub_begin, int32_t sub_count, hipStream_t stream);
+
 /* Workspace bytes skiparse_quant_fp8 needs for numel elements. */
 size_t skiparse_quant_fp8_workspace_bytes(int64_t numel);
 

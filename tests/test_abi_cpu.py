@@ -115,6 +115,62 @@ def test_attn_fwd_argument_errors():
     assert sk.lib().skiparse_attn_fwd(None, 1, 0x1000, 0x2000, 0x3000, 0x4000, 0.0, None, 0, 0, None) == sk.EINVAL
 
 
+def _fwd_lse_code(plan, dtype=sk.BF16, q=0x1000, k=0x100000000, v=0x200000000, o=0x300000000,
+                  lse=0x400000000, scale=0.0, sb=0, sc=0):
+    import ctypes
+    return sk.lib().skiparse_attn_fwd_lse(ctypes.byref(plan), dtype, q, k, v, o, lse, scale, sb, sc, None)
+
+
+def test_attn_fwd_lse_argument_errors():
+    """Validation failures of the training forward (nothing is launched)."""
+    p = sk.skiparse_plan_init(1, 2, 8, 8, 2, 128, 2, 0)
+    assert _fwd_lse_code(p, lse=0) == sk.EINVAL
+    assert _fwd_lse_code(p, lse=0x400000002) == sk.EINVAL              # misaligned
+    assert _fwd_lse_code(p, lse=0x1000 + 64) == sk.EINVAL              # overlaps q
+    assert _fwd_lse_code(p, dtype=sk.F32) == sk.EUNSUPPORTED
+    assert _fwd_lse_code(p, dtype=sk.FP8_E4M3) == sk.EUNSUPPORTED
+    assert _fwd_lse_code(p, sb=3, sc=2) == sk.EINVAL
+    assert _fwd_lse_code(p, scale=float("nan")) == sk.EINVAL
+    p96 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 96, 2, 0)
+    assert _fwd_lse_code(p96) == sk.EUNSUPPORTED
+
+
+def test_attn_bwd_argument_errors():
+    """Validation failures of the backward pass (nothing is launched)."""
+    import ctypes
+    L = sk.lib()
+    p = sk.skiparse_plan_init(1, 2, 8, 8, 2, 128, 2, 0)
+    rows = 1 * 2 * 8 * 8 * 2
+    need = sk.skiparse_attn_bwd_workspace_bytes(p)
+    assert need == rows * 4
+    G = 1 << 32
+    args = dict(q=1 * G, k=2 * G, v=3 * G, o=4 * G, do=5 * G, lse=6 * G, dq=7 * G, dk=8 * G, dv=9 * G, ws=10 * G,
+                wb=need, dtype=sk.BF16, sb=0, sc=0)
+
+    def code(plan=p, **kw):
+        a = dict(args, **kw)
+        return L.skiparse_attn_bwd(ctypes.byref(plan), a["dtype"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                                   a["dq"], a["dk"], a["dv"], 0.0, a["ws"], a["wb"], a["sb"], a["sc"], None)
+
+    assert code(dtype=sk.F32) == sk.EUNSUPPORTED
+    assert code(do=0) == sk.EINVAL
+    assert code(dk=7 * G + 8) == sk.EINVAL                           # misaligned
+    assert code(lse=6 * G + 2) == sk.EINVAL
+    assert code(ws=0) == sk.EWORKSPACE
+    assert code(wb=need - 4) == sk.EWORKSPACE
+    assert code(dq=1 * G + 256) == sk.EINVAL                         # dq overlaps q
+    assert code(dv=7 * G) == sk.EINVAL                               # dv overlaps dq
+    assert code(ws=9 * G) == sk.EINVAL                               # workspace overlaps dv
+    assert code(dk=6 * G) == sk.EINVAL                               # dk overlaps lse
+    assert code(sb=2, sc=3) == sk.EINVAL
+    p64 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 64, 2, 0)
+    assert code(plan=p64, wb=sk.skiparse_attn_bwd_workspace_bytes(p64)) == sk.EUNSUPPORTED
+    bad = sk.skiparse_plan_init(1, 2, 8, 8, 2, 128, 2, 0)
+    bad.n_sub = 3
+    assert code(plan=bad) == sk.EINVAL
+    assert sk.skiparse_attn_bwd_workspace_bytes(bad) == 0
+
+
 def test_quant_argument_errors():
     L = sk.lib()
     n = 1000
