@@ -247,6 +247,36 @@ def main():
                                "frac_hbm_peak": round(qbytes / (qms * 1e-3) / 1e9 / HBM_GBS, 4)}
         extras["fp8_e4m3"] = fp8
         del o8, codes
+        # training step of one layer: forward keeping the log-sum-exp, then the
+        # backward pass for a synthetic upstream gradient.  Backward FLOPs are
+        # counted as 2.5x the forward's (five n x n x d products: the S
+        # recompute, dP, dV, dQ, dK), whatever the kernels recompute beyond.
+        do_ = torch.from_numpy(wl.normal_tensor(w.shape, w.seed, 3)).to(torch.bfloat16).cuda()
+        train = {}
+        for mode, name in ((sk.MODE_TOKEN, "token"), (sk.MODE_GROUP, "group")):
+            pl = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, mode)
+            ot = torch.empty_like(q)
+            lse = torch.empty((B, T * H * W, nh), dtype=torch.float32, device="cuda")
+            grads = [torch.empty_like(q) for _ in range(3)]
+            ws = torch.empty(sk.skiparse_attn_bwd_workspace_bytes(pl), dtype=torch.uint8, device="cuda")
+            sk.skiparse_attn_fwd_lse(pl, sk.BF16, q, k, v, ot, lse, stream=stream)
+            sk.skiparse_attn_bwd(pl, sk.BF16, q, k, v, ot, do_, lse, *grads, workspace=ws, stream=stream)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            for _ in range(3):
+                sk.skiparse_attn_fwd_lse(pl, sk.BF16, q, k, v, ot, lse, stream=stream)
+            e[1].record(stream)
+            for _ in range(3):
+                sk.skiparse_attn_bwd(pl, sk.BF16, q, k, v, ot, do_, lse, *grads, workspace=ws, stream=stream)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            fms, bms = e[0].elapsed_time(e[1]) / 3, e[1].elapsed_time(e[2]) / 3
+            train[name] = {"fwd_lse_ms": round(fms, 3), "bwd_ms": round(bms, 3),
+                           "bwd_tflops": round(2.5 * pl.flops / (bms * 1e-3) / 1e12, 2),
+                           "bwd_frac_bf16_peak": round(2.5 * pl.flops / (bms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+            del ot, lse, grads, ws
+        extras["training_bf16"] = train
+        del do_
     result["extras"] = extras
 
     if not args.no_cpu_baseline:
