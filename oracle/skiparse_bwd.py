@@ -28,8 +28,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .skiparse_ref import (TOKEN, _members_for, default_scale, inverse_rearrange_literal, pad_tokens,
-                           padded_extent, real_token_mask, rearrange_literal)
+from .skiparse_ref import TOKEN, _members_for, default_scale, from_subsequences, subsequence_real_mask, to_subsequences
 
 
 def softmax_attention_bwd(q, k, v, do, scale, key_ok=None):
@@ -62,13 +61,11 @@ def skiparse_attention_bwd(q, k, v, do, kf: int, mode: int, scale=None):
     B, T, H, W, nh, d = q.shape
     mode = TOKEN if kf == 1 else mode
     scale = default_scale(d) if scale is None else scale
-    Hp, Wp = padded_extent(H, kf), padded_extent(W, kf)
-    qs, ks, vs, dos = (rearrange_literal(pad_tokens(np.asarray(x, np.float64), kf), kf, mode)
-                       for x in (q, k, v, do))
-    ok = rearrange_literal(real_token_mask(T, H, W, kf), kf, mode)[0, :, 0, :, 0]
+    qs, ks, vs, dos = (to_subsequences(np.asarray(x, np.float64), kf, mode) for x in (q, k, v, do))
+    ok = subsequence_real_mask(T, H, W, kf, mode)
     grads = [np.zeros_like(qs) for _ in range(3)]
     for b in range(B):
-        for s in range(kf * kf):
+        for s in range(qs.shape[1]):
             real = ok[s]
             if not real.any():
                 continue
@@ -79,7 +76,7 @@ def skiparse_attention_bwd(q, k, v, do, kf: int, mode: int, scale=None):
                 grads[0][b, s, h][real] = dq
                 grads[1][b, s, h][real] = dk
                 grads[2][b, s, h][real] = dv
-    return tuple(inverse_rearrange_literal(g, T, Hp, Wp, kf, mode)[:, :, :H, :W] for g in grads)
+    return tuple(from_subsequences(g, T, H, W, kf, mode) for g in grads)
 
 
 def attention_lse(q, k, kf: int, mode: int, scale=None):

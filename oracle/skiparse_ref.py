@@ -37,8 +37,26 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-TOKEN = 0  # token-wise pattern
-GROUP = 1  # group-wise pattern
+TOKEN = 0     # token-wise pattern
+GROUP = 1     # group-wise pattern
+TOKEN_1D = 2  # Skiparse-1D, token-wise, on the flattened (h, w) of each frame
+GROUP_1D = 3  # Skiparse-1D, group-wise
+
+
+def is_1d(mode: int) -> bool:
+    """Skiparse-1D: the skip pattern of one axis applied to the flattened
+    spatial sequence (OSP-Next summary, 技术新颖性 novelty: the 2D pattern is
+    the 1D one applied to each spatial axis, and the flattened 1D variant is
+    what it is compared with).  Reading: each frame's (h, w) is flattened to
+    l = h*W + w, the 1D rule runs along l with stride K = k*k (so the density
+    1/k^2 matches the 2D pattern), l is padded at its end to a multiple of K^2,
+    and every subsequence spans all T frames."""
+    return mode in (TOKEN_1D, GROUP_1D)
+
+
+def rule_of(mode: int) -> int:
+    """The per-axis rule (TOKEN or GROUP) a mode applies."""
+    return GROUP if mode in (GROUP, GROUP_1D) else TOKEN
 
 
 # ---------------------------------------------------------------------------
@@ -130,6 +148,19 @@ class Plan:
 def make_plan(B, T, H, W, heads, d, k, mode) -> Plan:
     mode = TOKEN if k == 1 else mode
     p = Plan(B, T, H, W, heads, d, k, mode)
+    if is_1d(mode):
+        # the flattened axis l = h*W + w of length L as the single row of a
+        # (T, 1, Lp) grid, stride K along it
+        K, L = k * k, H * W
+        p.Hp, p.Wp = 1, padded_extent(L, K)
+        p.sub_h, p.sub_w = 1, p.Wp // K
+        p.n_sub = K
+        p.sub_len_padded = T * p.sub_w
+        p.real_h = [1]
+        p.real_w = [real_extent(L, K, rule_of(mode), q) for q in range(K)]
+        p.sub_len = [T * r for r in p.real_w]
+        p.pairs = sum(n * n for n in p.sub_len) * B * heads
+        return p
     p.Hp, p.Wp = padded_extent(H, k), padded_extent(W, k)
     p.sub_h, p.sub_w = p.Hp // k, p.Wp // k
     p.n_sub = k * k
@@ -153,6 +184,17 @@ def gather_map(T: int, H: int, W: int, k: int, mode: int) -> np.ndarray:
     local grid (T, Hp/k, Wp/k) row-major.
     """
     mode = TOKEN if k == 1 else mode
+    if is_1d(mode):
+        # slot j = t * (Lp/K) + l' of subsequence q holds l = the l'-th index
+        # of coordinate q along the flattened axis
+        K, L = k * k, H * W
+        sw = padded_extent(L, K) // K
+        t = np.arange(T)[:, None]
+        G = np.full((K, T * sw), -1, dtype=np.int64)
+        for q in range(K):
+            l = spatial_of_local(np.arange(sw), q, K, rule_of(mode))[None, :]
+            G[q] = np.where((l < L) & (t >= 0), t * L + l, -1).reshape(-1)
+        return G
     Hp, Wp = padded_extent(H, k), padded_extent(W, k)
     sh, sw = Hp // k, Wp // k
     G = np.full((k * k, T * sh * sw), -1, dtype=np.int64)
@@ -232,6 +274,63 @@ def real_token_mask(T, H, W, k) -> np.ndarray:
     return m
 
 
+# --- Skiparse-1D: flatten, pad, reshape/transpose --------------------------
+
+def rearrange_1d_literal(x: np.ndarray, k: int, mode: int) -> np.ndarray:
+    """(B, T, Lp, heads, d), the flattened and padded frames, ->
+    (B, K, heads, T*Lp/K, d) with K = k*k:
+    token-wise 't (l' q) -> q (t l')', group-wise 't (lb q kl) -> q (t lb kl)'."""
+    B, T, Lp, nh, d = x.shape
+    K = k * k
+    if rule_of(mode) == TOKEN:
+        y = x.reshape(B, T, Lp // K, K, nh, d).transpose(0, 3, 4, 1, 2, 5)
+    else:
+        y = x.reshape(B, T, Lp // (K * K), K, K, nh, d).transpose(0, 3, 5, 1, 2, 4, 6)
+    return y.reshape(B, K, nh, -1, d)
+
+
+def inverse_rearrange_1d_literal(y: np.ndarray, T: int, Lp: int, k: int, mode: int) -> np.ndarray:
+    """Inverse of :func:`rearrange_1d_literal`."""
+    B, K, nh, _, d = y.shape
+    if rule_of(mode) == TOKEN:
+        x = y.reshape(B, K, nh, T, Lp // K, d).transpose(0, 3, 4, 1, 2, 5)
+    else:
+        x = y.reshape(B, K, nh, T, Lp // (K * K), K, d).transpose(0, 3, 4, 1, 5, 2, 6)
+    return x.reshape(B, T, Lp, nh, d)
+
+
+# --- both patterns: pad -> rearrange, and back -----------------------------
+
+def to_subsequences(x: np.ndarray, kf: int, mode: int) -> np.ndarray:
+    """Pad and rearrange (B, T, H, W, heads, d) into (B, n_sub, heads, L_sub, d)."""
+    mode = TOKEN if kf == 1 else mode
+    if not is_1d(mode):
+        return rearrange_literal(pad_tokens(x, kf), kf, mode)
+    B, T, H, W, nh, d = x.shape
+    Lp = padded_extent(H * W, kf * kf)
+    flat = np.zeros((B, T, Lp, nh, d), dtype=x.dtype)
+    flat[:, :, :H * W] = x.reshape(B, T, H * W, nh, d)
+    return rearrange_1d_literal(flat, kf, mode)
+
+
+def subsequence_real_mask(T: int, H: int, W: int, kf: int, mode: int) -> np.ndarray:
+    """(n_sub, L_sub) bool: which slots of each rearranged subsequence are real."""
+    m = np.ones((1, T, H, W, 1, 1), dtype=bool)
+    return to_subsequences(m, kf, mode)[0, :, 0, :, 0]
+
+
+def from_subsequences(y: np.ndarray, T: int, H: int, W: int, kf: int, mode: int) -> np.ndarray:
+    """Rearrange back and crop: (B, n_sub, heads, L_sub, d) -> (B, T, H, W, heads, d)."""
+    mode = TOKEN if kf == 1 else mode
+    if not is_1d(mode):
+        full = inverse_rearrange_literal(y, T, padded_extent(H, kf), padded_extent(W, kf), kf, mode)
+        return full[:, :, :H, :W]
+    B, nh, d = y.shape[0], y.shape[2], y.shape[4]
+    Lp = padded_extent(H * W, kf * kf)
+    flat = inverse_rearrange_1d_literal(y, T, Lp, kf, mode)
+    return flat[:, :, :H * W].reshape(B, T, H, W, nh, d)
+
+
 # ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
@@ -263,22 +362,18 @@ def skiparse_attention(q, k, v, kf: int, mode: int, scale=None) -> np.ndarray:
     B, T, H, W, nh, d = q.shape
     mode = TOKEN if kf == 1 else mode
     scale = default_scale(d) if scale is None else scale
-    Hp, Wp = padded_extent(H, kf), padded_extent(W, kf)
-    qs = rearrange_literal(pad_tokens(q, kf), kf, mode)
-    ks = rearrange_literal(pad_tokens(k_, kf), kf, mode)
-    vs = rearrange_literal(pad_tokens(v, kf), kf, mode)
-    ok = rearrange_literal(real_token_mask(T, H, W, kf), kf, mode)[0, :, 0, :, 0]
+    qs, ks, vs = (to_subsequences(x, kf, mode) for x in (q, k_, v))
+    ok = subsequence_real_mask(T, H, W, kf, mode)
     out = np.zeros_like(qs)
     for b in range(B):
-        for s in range(kf * kf):
+        for s in range(qs.shape[1]):
             if not ok[s].any():
                 continue  # a subsequence made only of padding has nothing to attend
             for h in range(nh):
                 o = softmax_attention(qs[b, s, h], ks[b, s, h], vs[b, s, h], scale, ok[s])
                 o[~ok[s]] = 0.0  # padded queries are discarded
                 out[b, s, h] = o
-    full = inverse_rearrange_literal(out, T, Hp, Wp, kf, mode)
-    return full[:, :, :H, :W]
+    return from_subsequences(out, T, H, W, kf, mode)
 
 
 # ---------------------------------------------------------------------------
@@ -295,7 +390,10 @@ def block_mask(T, H, W, k, mode) -> np.ndarray:
         for h in range(H):
             for w in range(W):
                 x = (t * H + h) * W + w
-                sub[x] = subsequence_coord(h, k, mode) * k + subsequence_coord(w, k, mode)
+                if is_1d(mode):   # the 1D rule on the flattened index, stride k*k
+                    sub[x] = subsequence_coord(h * W + w, k * k, rule_of(mode))
+                else:
+                    sub[x] = subsequence_coord(h, k, mode) * k + subsequence_coord(w, k, mode)
     return sub[:, None] == sub[None, :]
 
 

@@ -44,6 +44,10 @@ def load_golden(name):
     ("map_group_T1_H3_W5_k2.txt", 1, 3, 5, 2, ref.GROUP),
     ("map_group_T1_H8_W8_k2.txt", 1, 8, 8, 2, ref.GROUP),
     ("map_token_T2_H2_W2_k2.txt", 2, 2, 2, 2, ref.TOKEN),
+    ("map_token1d_T1_H2_W3_k2.txt", 1, 2, 3, 2, ref.TOKEN_1D),
+    ("map_group1d_T2_H3_W3_k2.txt", 2, 3, 3, 2, ref.GROUP_1D),
+    ("map_token1d_T1_H4_W5_k2.txt", 1, 4, 5, 2, ref.TOKEN_1D),
+    ("map_group1d_T1_H4_W5_k2.txt", 1, 4, 5, 2, ref.GROUP_1D),
 ])
 def test_golden_maps(fname, T, H, W, k, mode):
     np.testing.assert_array_equal(ref.gather_map(T, H, W, k, mode), load_golden(fname))
