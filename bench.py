@@ -277,6 +277,23 @@ def main():
             del ot, lse, grads, ws
         extras["training_bf16"] = train
         del do_
+        # Skiparse-1D on the same shape (the 1D rule on each frame's flattened
+        # (h, w), stride k*k: the variant the 2D pattern is compared with)
+        one_d = {}
+        o1d = torch.empty_like(q)
+        for mode, name in ((sk.MODE_TOKEN_1D, "token"), (sk.MODE_GROUP_1D, "group")):
+            pl = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, mode)
+            sk.skiparse_attn_fwd(pl, sk.BF16, q, k, v, o1d, stream=stream)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            for _ in range(3):
+                sk.skiparse_attn_fwd(pl, sk.BF16, q, k, v, o1d, stream=stream)
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            ms = e[0].elapsed_time(e[1]) / 3
+            one_d[name] = {"ms": round(ms, 3), "tflops": round(pl.flops / (ms * 1e-3) / 1e12, 2), "pairs": int(pl.pairs)}
+        extras["skiparse_1d_bf16"] = one_d
+        del o1d
     result["extras"] = extras
 
     if not args.no_cpu_baseline:

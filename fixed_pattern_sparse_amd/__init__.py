@@ -47,6 +47,8 @@ EWORKSPACE = -4
 
 MODE_TOKEN = 0
 MODE_GROUP = 1
+MODE_TOKEN_1D = 2
+MODE_GROUP_1D = 3
 
 F32 = 0
 BF16 = 1
@@ -91,6 +93,9 @@ class SkiparsePlan(ctypes.Structure):
         return 4 * self.d * self.pairs
 
     def sub_lengths(self):
+        """Real tokens per subsequence, in subsequence order."""
+        if self.mode in (MODE_TOKEN_1D, MODE_GROUP_1D):
+            return [self.T * self.real_w[q] for q in range(self.n_sub)]
         k = self.k
         return [self.T * self.real_h[p] * self.real_w[q] for p in range(k) for q in range(k)]
 

@@ -29,11 +29,12 @@ int ok() {
   return SKIPARSE_OK;
 }
 
-// Real local extent on one axis for coordinate p (any-resolution rule: the
-// real members are a prefix of the local axis).
-int32_t real_extent(int32_t n, int32_t k, int32_t mode, int32_t p) {
+// Real local extent on one axis of stride k for coordinate p (any-resolution
+// rule: the real members are a prefix of the local axis); rule 0 token-wise,
+// 1 group-wise.
+int32_t real_extent(int32_t n, int32_t k, int32_t rule, int32_t p) {
   if (k == 1) return n;
-  if (mode == SKIPARSE_MODE_TOKEN) return n / k + (p < n % k ? 1 : 0);
+  if (rule == 0) return n / k + (p < n % k ? 1 : 0);
   const int32_t kk = k * k;
   int32_t r = n % kk - p * k;
   r = r < 0 ? 0 : (r > k ? k : r);
@@ -61,18 +62,28 @@ int check_plan(const skiparse_plan* p) {
   return SKIPARSE_OK;
 }
 
+bool is_1d(int32_t mode) { return mode == SKIPARSE_MODE_TOKEN_1D || mode == SKIPARSE_MODE_GROUP_1D; }
+
+// Strides along the kernels' h and w axes.  Skiparse-1D runs along each
+// frame's flattened l = h*W + w (grid (T, 1, H*W)) with stride k*k.
+int32_t stride_h(const skiparse_plan& p) { return is_1d(p.mode) ? 1 : p.k; }
+int32_t stride_w(const skiparse_plan& p) { return is_1d(p.mode) ? p.k * p.k : p.k; }
+
 void make_geom(const skiparse_plan& p, Geom& g) {
   g.T = p.T;
-  g.H = p.H;
-  g.W = p.W;
-  g.k = p.k;
-  g.mode = p.mode;
-  g.div_k = make_fastdiv((uint32_t)p.k);
+  g.H = is_1d(p.mode) ? 1 : p.H;
+  g.W = is_1d(p.mode) ? p.H * p.W : p.W;
+  g.kh = stride_h(p);
+  g.kw = stride_w(p);
+  g.rule = (p.mode == SKIPARSE_MODE_GROUP || p.mode == SKIPARSE_MODE_GROUP_1D) ? 1 : 0;
+  g.div_kh = make_fastdiv((uint32_t)g.kh);
+  g.div_kw = make_fastdiv((uint32_t)g.kw);
 }
 
 SubGeom make_sub(const skiparse_plan& p, int s) {
   SubGeom sg;
-  const int pp = s / p.k, qq = s % p.k;
+  const int kw = stride_w(p);
+  const int pp = s / kw, qq = s % kw;
   const int32_t hr = p.real_h[pp], wr = p.real_w[qq];
   sg.n = p.T * hr * wr;
   sg.p = pp;
@@ -102,9 +113,16 @@ int skiparse_plan_init(skiparse_plan* plan, int32_t B, int32_t T, int32_t H, int
   if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || d < 1)
     return fail(SKIPARSE_EINVAL, "every extent must be >= 1 (B=%d T=%d H=%d W=%d heads=%d d=%d)", B, T, H, W, heads, d);
   if (k < 1 || k > SKIPARSE_MAX_K) return fail(SKIPARSE_EINVAL, "k=%d outside [1, %d]", k, SKIPARSE_MAX_K);
-  if (mode != SKIPARSE_MODE_TOKEN && mode != SKIPARSE_MODE_GROUP) return fail(SKIPARSE_EINVAL, "mode=%d is not token (0) or group (1)", mode);
+  if (mode < SKIPARSE_MODE_TOKEN || mode > SKIPARSE_MODE_GROUP_1D)
+    return fail(SKIPARSE_EINVAL, "mode=%d is not token (0), group (1), token-1D (2) or group-1D (3)", mode);
+  const bool one_d = k > 1 && (mode == SKIPARSE_MODE_TOKEN_1D || mode == SKIPARSE_MODE_GROUP_1D);
+  if (one_d && k * k > SKIPARSE_MAX_K)
+    return fail(SKIPARSE_EINVAL, "the 1-D modes hold k*k subsequences in the plan's real_w[%d]: k <= 2 (k=%d)", SKIPARSE_MAX_K, k);
   const int64_t kk = (int64_t)k * k;
-  const int64_t Hp = (H + kk - 1) / kk * kk, Wp = (W + kk - 1) / kk * kk;
+  // the grid the pattern runs on: (T, H, W), or (T, 1, H*W) for Skiparse-1D
+  const int64_t gh = one_d ? 1 : H, gw = one_d ? (int64_t)H * W : W;
+  const int64_t sh = one_d ? 1 : k, swd = one_d ? kk : k;   // strides along the grid's axes
+  const int64_t Hp = (gh + sh * sh - 1) / (sh * sh) * (sh * sh), Wp = (gw + swd * swd - 1) / (swd * swd) * (swd * swd);
   const int64_t tokens = (int64_t)T * H * W;
   const int64_t padded = (int64_t)T * Hp * Wp;
   if (padded >= (int64_t(1) << 31)) return fail(SKIPARSE_EINVAL, "T*Hp*Wp = %lld must stay below 2^31", (long long)padded);
@@ -123,18 +141,17 @@ int skiparse_plan_init(skiparse_plan* plan, int32_t B, int32_t T, int32_t H, int
   plan->mode = k == 1 ? SKIPARSE_MODE_TOKEN : mode;
   plan->Hp = (int32_t)Hp;
   plan->Wp = (int32_t)Wp;
-  plan->sub_h = (int32_t)(Hp / k);
-  plan->sub_w = (int32_t)(Wp / k);
+  plan->sub_h = (int32_t)(Hp / sh);
+  plan->sub_w = (int32_t)(Wp / swd);
   plan->n_sub = (int32_t)kk;
   plan->sub_len_padded = (int64_t)T * plan->sub_h * plan->sub_w;
-  for (int p = 0; p < k; ++p) {
-    plan->real_h[p] = real_extent(H, k, plan->mode, p);
-    plan->real_w[p] = real_extent(W, k, plan->mode, p);
-  }
+  const int32_t rule = (plan->mode == SKIPARSE_MODE_GROUP || plan->mode == SKIPARSE_MODE_GROUP_1D) ? 1 : 0;
+  for (int p = 0; p < sh; ++p) plan->real_h[p] = real_extent((int32_t)gh, (int32_t)sh, rule, p);
+  for (int q = 0; q < swd; ++q) plan->real_w[q] = real_extent((int32_t)gw, (int32_t)swd, rule, q);
   double pairs = 0;
   int64_t pairs_i = 0;
-  for (int p = 0; p < k; ++p)
-    for (int q = 0; q < k; ++q) {
+  for (int p = 0; p < sh; ++p)
+    for (int q = 0; q < swd; ++q) {
       const int64_t n = (int64_t)T * plan->real_h[p] * plan->real_w[q];
       pairs += (double)n * n;
       pairs_i += n * n;
@@ -152,7 +169,8 @@ int skiparse_plan_index_map(const skiparse_plan* plan, int32_t* host_gather) {
   const int64_t L = plan->sub_len_padded;
   for (int s = 0; s < plan->n_sub; ++s) {
     const SubGeom sg = make_sub(*plan, s);
-    const int32_t hr = plan->real_h[s / plan->k], wr = plan->real_w[s % plan->k];
+    const int32_t kw = stride_w(*plan);
+    const int32_t hr = plan->real_h[s / kw], wr = plan->real_w[s % kw];
     int32_t* row = host_gather + (int64_t)s * L;
     int64_t x = 0;
     for (int32_t t = 0; t < plan->T; ++t)

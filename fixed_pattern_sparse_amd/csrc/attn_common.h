@@ -51,10 +51,10 @@ __device__ __forceinline__ void build_row_tables(const AttnArgs& a, const SubGeo
   const int hr = th_end / a.g.T;
   for (int x = threadIdx.x; x < th_end; x += nthreads) {
     const int t = x / hr;
-    const int hh = (int)axis_of_local((uint32_t)(x - t * hr), (uint32_t)sg.p, a.g);
+    const int hh = (int)h_of_local((uint32_t)(x - t * hr), (uint32_t)sg.p, a.g);
     rowbase[x] = (t * a.g.H + hh) * a.g.W;
   }
-  for (int x = threadIdx.x; x < wr; x += nthreads) colmap[x] = (int)axis_of_local((uint32_t)x, (uint32_t)sg.q, a.g);
+  for (int x = threadIdx.x; x < wr; x += nthreads) colmap[x] = (int)w_of_local((uint32_t)x, (uint32_t)sg.q, a.g);
   __syncthreads();
 }
 

@@ -1,13 +1,18 @@
-// Index function of the Skiparse-2D rearrange, shared by the host plan and
-// every device kernel of libskiparse.
+// Index function of the Skiparse rearrange, shared by the host plan and every
+// device kernel of libskiparse.
 //
-// Rule (OSP-Next summary, 核心方法 core method; 方法步骤详情 method steps):
-//   token-wise:  h = h' * k + p                      (pixel unshuffle)
-//   group-wise:  h = (h' / k) * k^2 + p * k + h' % k  (patch unshuffle, block index mod k)
-// and the same along w with q.  The real tokens of subsequence s = p*k + q fill
-// the prefix box [0,T) x [0,Hr(p)) x [0,Wr(q)) of its local grid, so the
-// kernels enumerate a subsequence compactly, j = (t * Hr + h') * Wr + w',
-// j in [0, T*Hr*Wr), and never touch padding.
+// Rule along one axis with stride k (OSP-Next summary, 核心方法 core method;
+// 方法步骤详情 method steps):
+//   token-wise:  x = x' * k + p                      (pixel unshuffle)
+//   group-wise:  x = (x' / k) * k^2 + p * k + x' % k  (patch unshuffle, block index mod k)
+// Skiparse-2D applies it to h (stride kh = k, coordinate p) and w (kw = k, q).
+// Skiparse-1D applies it to each frame's flattened l = h*W + w with stride
+// K = k*k (技术新颖性 novelty: the 2D pattern is the 1D one per axis): the
+// kernels see the grid (T, 1, H*W) with kh = 1 and kw = K.  Either way the
+// real tokens of subsequence s = p*kw + q fill the prefix box
+// [0,T) x [0,Hr(p)) x [0,Wr(q)) of its local grid, so the kernels enumerate a
+// subsequence compactly, j = (t * Hr + h') * Wr + w', j in [0, T*Hr*Wr), and
+// never touch padding.
 #pragma once
 
 #include <stdint.h>
@@ -61,21 +66,24 @@ struct SubGeom {
   FastDiv div_w;     // division by wr      (div_w.d == wr)
 };
 
-// Call-wide geometry.
+// Call-wide geometry: the grid the kernels index (T, H, W; for Skiparse-1D
+// (T, 1, H*W)) and the stride along each axis.
 struct Geom {
   int32_t T, H, W;
-  int32_t k;
-  int32_t mode;      // 0 token-wise, 1 group-wise (k == 1 behaves as token-wise)
-  FastDiv div_k;
+  int32_t kh, kw;    // strides along h and w (1 leaves the axis whole)
+  int32_t rule;      // 0 token-wise, 1 group-wise (a stride of 1 behaves as either)
+  FastDiv div_kh, div_kw;
 };
 
-// Spatial index of local coordinate xl on an axis with subsequence coordinate p.
-SK_HD uint32_t axis_of_local(uint32_t xl, uint32_t p, const Geom& g) {
-  if (g.mode == 0) return xl * (uint32_t)g.k + p;
-  uint32_t blk = fdiv(xl, g.div_k);
-  uint32_t kk = (uint32_t)g.k;
-  return blk * kk * kk + p * kk + (xl - blk * kk);
+// Spatial index of local coordinate xl on an axis of stride k and
+// subsequence coordinate p.
+SK_HD uint32_t axis_of_local(uint32_t xl, uint32_t p, uint32_t k, const FastDiv& div_k, int32_t rule) {
+  if (rule == 0) return xl * k + p;
+  uint32_t blk = fdiv(xl, div_k);
+  return blk * k * k + p * k + (xl - blk * k);
 }
+SK_HD uint32_t h_of_local(uint32_t xl, uint32_t p, const Geom& g) { return axis_of_local(xl, p, (uint32_t)g.kh, g.div_kh, g.rule); }
+SK_HD uint32_t w_of_local(uint32_t xl, uint32_t q, const Geom& g) { return axis_of_local(xl, q, (uint32_t)g.kw, g.div_kw, g.rule); }
 
 // Flat token index (t*H + h)*W + w of compact member j of subsequence s.
 SK_HD uint32_t token_of(uint32_t j, const SubGeom& s, const Geom& g) {
@@ -83,8 +91,8 @@ SK_HD uint32_t token_of(uint32_t j, const SubGeom& s, const Geom& g) {
   uint32_t r = j - t * s.div_hw.d;
   uint32_t hl = fdiv(r, s.div_w);
   uint32_t wl = r - hl * s.div_w.d;
-  uint32_t h = axis_of_local(hl, (uint32_t)s.p, g);
-  uint32_t w = axis_of_local(wl, (uint32_t)s.q, g);
+  uint32_t h = h_of_local(hl, (uint32_t)s.p, g);
+  uint32_t w = w_of_local(wl, (uint32_t)s.q, g);
   return (t * (uint32_t)g.H + h) * (uint32_t)g.W + w;
 }
 

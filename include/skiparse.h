@@ -53,7 +53,16 @@ typedef enum {
 
 typedef enum {
   SKIPARSE_MODE_TOKEN = 0,     /* token-wise pattern */
-  SKIPARSE_MODE_GROUP = 1      /* group-wise pattern (ignored when k == 1) */
+  SKIPARSE_MODE_GROUP = 1,     /* group-wise pattern (ignored when k == 1) */
+  /* Skiparse-1D, the variant the 2D pattern is compared with (OSP-Next
+   * summary, novelty): the same two rules on each frame's flattened spatial
+   * index l = h*W + w, stride k*k (density 1/k^2 as in 2D), l padded at its
+   * end to a multiple of k^4; every subsequence spans all T frames.  The plan
+   * then describes the grid (T, 1, H*W): Hp = 1, Wp = padded length,
+   * sub_h = 1, sub_w = Wp / k^2, real_h[0] = 1, real_w[q] for q < k^2, and
+   * subsequence s = q.  k <= 2 (k^2 extents must fit real_w). */
+  SKIPARSE_MODE_TOKEN_1D = 2,
+  SKIPARSE_MODE_GROUP_1D = 3
 } skiparse_mode;
 
 typedef enum {
@@ -65,14 +74,16 @@ typedef enum {
 /*
  * Geometry of one attention call, filled by skiparse_plan_init.  Plain data:
  * the caller owns it and may copy it.
- *   Hp, Wp          H, W rounded up to a multiple of k*k (any-resolution rule)
+ *   Hp, Wp          H, W rounded up to a multiple of k*k (any-resolution
+ *                   rule); the 1-D modes: see skiparse_mode
  *   sub_h, sub_w    local grid of a subsequence: Hp / k rows, Wp / k columns;
  *                   every subsequence spans all T frames
  *   sub_len_padded  T * sub_h * sub_w slots per subsequence
  *   real_h[p]       real local rows of subsequences with row coordinate p
  *   real_w[q]       real local columns of subsequences with column coordinate q
  *                   The real tokens of subsequence s = p*k + q fill the prefix
- *                   box [0,T) x [0,real_h[p]) x [0,real_w[q]) of its local grid.
+ *                   box [0,T) x [0,real_h[p]) x [0,real_w[q]) of its local grid
+ *                   (the 1-D modes: s = q, local grid (T, 1, sub_w)).
  *   pairs           computed (real x real, same subsequence) query-key pairs
  *                   of a whole call: sum_s n_s^2 * B * heads; 4 * d * pairs
  *                   is the call's algorithmic FLOP count

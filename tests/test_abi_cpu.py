@@ -56,6 +56,28 @@ def test_plan_matches_oracle(shape, k, mode):
     assert p.mode == o.mode
 
 
+@pytest.mark.parametrize("k", [1, 2])
+@pytest.mark.parametrize("mode", [2, 3])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_plan_1d_matches_oracle(shape, k, mode):
+    B, T, H, W, nh, d = shape
+    p = sk.skiparse_plan_init(B, T, H, W, nh, d, k, mode)
+    o = ref.make_plan(B, T, H, W, nh, d, k, mode)
+    assert (p.Hp, p.Wp, p.sub_h, p.sub_w, p.n_sub, p.sub_len_padded) == (o.Hp, o.Wp, o.sub_h, o.sub_w, o.n_sub, o.sub_len_padded)
+    assert list(p.real_h)[:len(o.real_h)] == o.real_h and list(p.real_w)[:len(o.real_w)] == o.real_w
+    assert p.pairs == o.pairs and p.mode == o.mode
+    assert p.sub_lengths() == o.sub_len
+
+
+@pytest.mark.parametrize("k", [1, 2])
+@pytest.mark.parametrize("mode", [2, 3])
+@pytest.mark.parametrize("T,H,W", [(1, 2, 3), (2, 3, 3), (1, 4, 5), (3, 9, 7), (2, 21, 45), (1, 45, 80), (1, 1, 1),
+                                   (4, 13, 2)])
+def test_host_index_map_1d_bit_exact(T, H, W, k, mode):
+    p = sk.skiparse_plan_init(1, T, H, W, 1, 64, k, mode)
+    np.testing.assert_array_equal(sk.skiparse_plan_index_map(p), ref.gather_map(T, H, W, k, mode))
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 7, 8])
 @pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("T,H,W", [(1, 4, 4), (2, 8, 8), (1, 3, 5), (3, 9, 7), (2, 21, 45), (1, 45, 80),
@@ -74,7 +96,8 @@ def test_host_index_map_at_720p_shape():
 
 @pytest.mark.parametrize("args", [
     (0, 1, 1, 1, 1, 64, 2, 0), (1, 1, 1, 1, 1, 64, 0, 0), (1, 1, 1, 1, 1, 64, 9, 0),
-    (1, 1, 1, 1, 1, 64, 2, 2), (1, -1, 4, 4, 1, 64, 2, 0), (1, 1, 70000, 70000, 1, 64, 1, 0),
+    (1, 1, 1, 1, 1, 64, 2, 4), (1, -1, 4, 4, 1, 64, 2, 0), (1, 1, 70000, 70000, 1, 64, 1, 0),
+    (1, 1, 4, 4, 1, 64, 3, 2),   # 1-D mode with k*k = 9 > 8 subsequences
 ])
 def test_plan_init_rejects(args):
     with pytest.raises(sk.SkiparseError) as e:
