@@ -37,6 +37,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
@@ -234,6 +235,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     auto exps = [&]() {
       const float mneg = -m_run;
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -242,9 +244,12 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
           for (int e = 0; e < 4; ++e) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][cc * 8 + 2 * e], c, mneg));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][cc * 8 + 2 * e + 1], c, mneg));
-            ls[mb * 2 + cc] += p0 + p1;
-            pk[mb][cc][2 * e] = (__bf16)p0;
-            pk[mb][cc][2 * e + 1] = (__bf16)p1;
+            // the row sum takes the bf16-rounded p the PV product uses, two
+            // terms per dot2 instruction
+            bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+            ls[mb * 2 + cc] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[mb * 2 + cc], false);
+            pk[mb][cc][2 * e] = pp[0];
+            pk[mb][cc][2 * e + 1] = pp[1];
           }
       lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };

@@ -2,8 +2,9 @@
 pass (dQ, dK, dV) through the C ABI, against the oracle's float64 gradients
 (oracle/skiparse_bwd.py) on the same bf16 inputs.
 
-Bars.  Log-sum-exp: within 2e-4 (absolute; it is formed from the fp32 running
-max and sum).  Gradients: max|g - g_ref| <= 2e-2 * max|g_ref| per tensor, the
+Bars.  Log-sum-exp: within 2^-9 (absolute): the kernel's denominator sums
+the bf16-rounded weights its PV product uses, each within 2^-9 relative of the
+exact one, so log l is within 2^-9 of the exact value.  Gradients: max|g - g_ref| <= 2e-2 * max|g_ref| per tensor, the
 bf16 bar taken relative to the tensor's largest entry (gradients are often
 well below 1, where a max(1, .) normalisation would not test anything).  The
 kernels see the bf16 output O of the forward pass, the oracle the exact one;
@@ -25,7 +26,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 TOL = 2e-2
-LSE_TOL = 2e-4
+LSE_TOL = 2.0 ** -9
 
 
 def rel_err(got, want):
