@@ -17,11 +17,12 @@
 //   attn_bwd_dq_kernel   8 waves x 32 queries hold Q and dO fragments; key
 //                        tiles of 32 rows stream K and V through LDS;
 //                        S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T;
-//   attn_bwd_dkv_kernel  8 waves x 32 keys hold K (and V) fragments; query
-//                        tiles of 32 rows stream Q and dO (with L and D);
-//                        S = Q K^T + (-L/c), P = exp2(c S); the dV instance
-//                        does dV^T += dO^T P, the dK instance
-//                        dP = dO V^T + (-D), dK^T += Q^T (P * dP).
+//   attn_bwd_dkv_fused_kernel
+//                        8 waves x 32 keys hold K fragments, the work-group's
+//                        V rows sit in LDS; query tiles of 32 rows stream Q
+//                        and dO (with L and D); S = Q K^T + (-L/c),
+//                        P = exp2(c S), dV^T += dO^T P, dP = dO V^T + (-D),
+//                        dK^T += Q^T (P * dP).
 // Per-query L and D enter the dK/dV kernel through the MFMA accumulator's
 // initial value, so they cost no registers of their own.  Each staged tile is
 // read both row-major (ds_read_b128, 16 rows at one chunk) and transposed
@@ -55,6 +56,7 @@ static_assert(kBT * kCH == kThreads, "one chunk per thread and matrix per tile")
 
 __shared__ __attribute__((aligned(16))) char gA[2 * kTileB];   // K (dQ kernel) or Q (dK/dV kernel)
 __shared__ __attribute__((aligned(16))) char gB[2 * kTileB];   // V (dQ kernel) or dO (dK/dV kernel)
+__shared__ __attribute__((aligned(16))) char gVk[kBM * kRowB];  // dK/dV kernel: V rows of its 256 keys
 __shared__ __attribute__((aligned(16))) float gL[2 * kBT];     // dK/dV kernel: -L/c per query row
 __shared__ __attribute__((aligned(16))) float gDn[2 * kBT];    // dK/dV kernel: -D per query row
 __shared__ int32_t gTokB[kTokCap];
@@ -255,12 +257,15 @@ attn_bwd_dq_kernel(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK or dV: keys fixed, query tiles streamed
+// dK and dV together: keys fixed, query tiles streamed.  K fragments stay in
+// registers; the work-group's V rows are staged once in LDS and read as the B
+// operand of dP, which keeps the two accumulator sets within two waves per
+// SIMD.  Rows come from the index function (the V block leaves no room for
+// the token table).
 // ---------------------------------------------------------------------------
 
-template <int ROWS, bool DK>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_bwd_dkv_kernel(const AttnArgs a) {
+attn_bwd_dkv_fused_kernel(const AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -276,15 +281,13 @@ attn_bwd_dkv_kernel(const AttnArgs a) {
   const int64_t rs = a.row_stride;
   const char* __restrict__ qb = (const char*)((const __bf16*)a.q + base);
   const char* __restrict__ db_ = (const char*)((const __bf16*)a.dout + base);
+  const char* __restrict__ vb = (const char*)((const __bf16*)a.v + base);
   const float c = a.scale_log2;
   const float inv_c = 1.0f / c;
+  Rows<0> rows(a, sg, n);
 
-  Rows<ROWS> rows(a, sg, n);
-  rows.build(tid);
   const int lrow = tid / kCH, lslot = tid % kCH;
   const int sw_st = (lslot ^ uswz(lrow)) * 16;
-  // loader: one chunk of Q and of dO per thread; slot-0 threads also bring
-  // the row's -L/c and -D (+inf / 0 past the end, so those rows weigh zero)
   auto fetch = [&](int tile, uint4& qx, uint4& dx, float& ln, float& dn) {
     const int j = tile * kBT + lrow;
     const int t = rows.tok(j);
@@ -309,27 +312,36 @@ attn_bwd_dkv_kernel(const AttnArgs a) {
   float ln = 0.f, dn = 0.f;
   fetch(0, qx, dx, ln, dn);
 
-  // the lane's key: K (and V) fragments as B operands
-  const int jk = wi.qtile * kBM + wave * 32 + l32;
+  // V rows of the work-group's 256 keys (clamped past the end), swizzled like
+  // the tiles: key row r at chunk c ^ uswz(r)
+  const int key0 = wi.qtile * kBM;
+#pragma unroll
+  for (int i = 0; i < kBM * kCH / kThreads; ++i) {
+    const int r = lrow + i * kBT;
+    const int64_t off = (int64_t)rows.tok(key0 + r) * rs * 2 + lslot * 16;
+    *(uint4*)(gVk + r * kRowB + (lslot ^ uswz(r)) * 16) = *(const uint4*)(vb + off);
+  }
+
+  const int jk = key0 + wave * 32 + l32;
   const bool kok = jk < n;
   const int64_t koff = (int64_t)rows.tok(jk) * rs;
-  bf16x8 kf[KK], vf[KK];
+  bf16x8 kf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     kf[kk] = *(const bf16x8*)((const __bf16*)a.k + base + koff + kk * 16 + hl * 8);
     __asm__ volatile("" : "+v"(kf[kk]));
-    if constexpr (DK) {
-      vf[kk] = *(const bf16x8*)((const __bf16*)a.v + base + koff + kk * 16 + hl * 8);
-      __asm__ volatile("" : "+v"(vf[kk]));
-    }
   }
+  const char* sVk = gVk + wave * 32 * kRowB;   // the wave's 32 key rows
 
   stash(0, qx, dx, ln, dn);
   __syncthreads();
 
-  floatx16 acc[DB];
+  floatx16 accK[DB], accV[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = floatx16{};
+  for (int db = 0; db < DB; ++db) {
+    accK[db] = floatx16{};
+    accV[db] = floatx16{};
+  }
 
   for (int j = 0; j < nq; ++j) {
     const int buf = j & 1;
@@ -337,8 +349,7 @@ attn_bwd_dkv_kernel(const AttnArgs a) {
     if (more) fetch(j + 1, qx, dx, ln, dn);
     const char* sQ = gA + buf * kTileB;
     const char* sD = gB + buf * kTileB;
-    // S = Q K^T - L/c: the accumulator starts at -L/c of its query row
-    // (rows 8(i/4) + 4hl + i%4), so P = exp2(c * S)
+    // S = Q K^T - L/c (accumulator starting at -L/c of its query row)
     floatx16 s;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -353,43 +364,43 @@ attn_bwd_dkv_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] * c);
     bf16x8 pb[2];
-    if constexpr (!DK) {
-      pack_b(p, pb);
-      // dV^T += dO^T P
+    pack_b(p, pb);
+    // dV^T += dO^T P
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols(sD, lane, hl, db, cc), pb[cc], acc[db], 0, 0, 0);
-    } else {
-      // dP - D = dO V^T - D, the accumulator starting at -D of its query row
-      floatx16 dp;
+      for (int cc = 0; cc < 2; ++cc)
+        accV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols(sD, lane, hl, db, cc), pb[cc], accV[db], 0, 0, 0);
+    // dP - D = dO V^T - D; V^T of the lane's key from LDS
+    floatx16 dp;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const floatx4 d4 = *(const floatx4*)(gDn + buf * kBT + g * 8 + hl * 4);
+    for (int g = 0; g < 4; ++g) {
+      const floatx4 d4 = *(const floatx4*)(gDn + buf * kBT + g * 8 + hl * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dp[g * 4 + e] = d4[e];
-      }
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sD, l32, hl, kk), vf[kk], dp, 0, 0, 0);
-      float ds[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = p[i] * dp[i];
-      pack_b(ds, pb);
-      // dK^T += Q^T dS
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols(sQ, lane, hl, db, cc), pb[cc], acc[db], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) dp[g * 4 + e] = d4[e];
     }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sD, l32, hl, kk), frag_rows(sVk, l32, hl, kk), dp, 0, 0, 0);
+    // dS = P * (dP - D), with P taken back from its bf16 copy (the value the
+    // dV product used), so the fp32 P need not stay live
+    float ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ds[i] = (float)pb[i >> 3][i & 7] * dp[i];
+    bf16x8 dsb[2];
+    pack_b(ds, dsb);
+    // dK^T += Q^T dS
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        accK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols(sQ, lane, hl, db, cc), dsb[cc], accK[db], 0, 0, 0);
     if (more) stash(buf ^ 1, qx, dx, ln, dn);
     __syncthreads();
   }
   if (kok) {
-    __bf16* dst = (__bf16*)(DK ? a.dk : a.dv) + base + koff;
-    store_rows_t(dst, acc, DK ? a.scale : 1.0f, hl);
+    store_rows_t((__bf16*)a.dk + base + koff, accK, a.scale, hl);
+    store_rows_t((__bf16*)a.dv + base + koff, accV, 1.0f, hl);
   }
 }
 
@@ -410,15 +421,11 @@ hipError_t launch_attn_bwd(AttnArgs a, int B, int d, hipStream_t stream) {
   if (a.total_tiles == 0) return hipGetLastError();
   const bool table = token_table_ok(a, (int64_t)a.row_stride * 2, kTokCap);
   const dim3 grid(a.total_tiles), block(kThreads);
-  if (table) {
+  if (table)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<2>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<2, false>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<2, true>), grid, block, 0, stream, a);
-  } else {
+  else
     hipLaunchKernelGGL((attn_bwd_dq_kernel<0>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<0, false>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<0, true>), grid, block, 0, stream, a);
-  }
+  hipLaunchKernelGGL(attn_bwd_dkv_fused_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
