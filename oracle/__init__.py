@@ -26,6 +26,9 @@ Modules:
   for an upstream dO (the chain rule through softmax attention, per
   subsequence), the per-query log-sum-exp, and sampled-row evaluators for
   full-size shapes.
+* :mod:`oracle.block_ref` -- one fp8 attention block around the sparse
+  attention (per-tensor e4m3 input, QKV projections, 3-axis rotary embedding,
+  attention, output projection), every product in float64.
 * :mod:`oracle.fp8_ref` -- OCP FP8 E4M3 codec from the format definition and the
   per-tensor amax scale rule.
 * :mod:`oracle.cpu_baseline` -- the same algorithm in fp32 numpy/BLAS, timed
@@ -34,6 +37,8 @@ Modules:
 Every function is pinned by ``-m "not gpu"`` tests against values the pages
 and the mathematics fix (hand-derived golden maps, torch's pixel_unshuffle,
 textbook softmax attention, closed forms, invariants; for the gradients:
-finite differences of the forward oracle and torch's float64 autograd).  No function here is
+finite differences of the forward oracle and torch's float64 autograd; for
+the block: the rotary embedding as complex rotation, its relative-position
+property, torch's linear layers with the codec bypassed).  No function here is
 "parity unpinned".
 """
