@@ -9,7 +9,8 @@ HBM.  Printed as ONE JSON line: TFLOP/s counting only computed (real x real,
 same subsequence) pairs, ms per step, the roofline of the attention kernel
 (average launch duration from HIP events on the launch stream), the oracle's
 CPU baseline on a bounded sample, and extras: ms per layer, the same kernel at
-k = 1 (full attention) and the fp8 path.
+k = 1 (full attention), the fp8 path, a training step (forward with the
+log-sum-exp, backward) and Skiparse-1D.
 """
 
 from __future__ import annotations

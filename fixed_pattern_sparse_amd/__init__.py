@@ -19,12 +19,20 @@ The names mirror the C ABI in include/skiparse.h:
     skiparse_quant_fp8_workspace_bytes(numel)
     skiparse_quant_fp8(x, y, scale, fp8_max=448.0, eps=1e-12,
                        workspace=None, stream=None)
+    skiparse_block_workspace_bytes(plan)
+    skiparse_block_fwd_fp8(plan, x, w_qkvo, w_scales, y, rope_theta=10000.0,
+                           rope_dims=None, workspace=None, stream=None)
+    skiparse_gemm_fp8(x, w, sx, sw, y, stream=None)
+    skiparse_rope_fp8_workspace_bytes(plan)
+    skiparse_rope_fp8(plan, x, y, scale, rope_theta=10000.0, rope_dims=None,
+                      workspace=None, stream=None)
     skiparse_last_error()
 
 plus conveniences that allocate their outputs with torch:
 ``attention``, ``attention_fp8``, ``quantize_fp8``, ``attention_train``
-(output and log-sum-exp), ``attention_bwd`` (dq, dk, dv) and
-``SkiparseAttention`` (a torch.autograd.Function over the last two).
+(output and log-sum-exp), ``attention_bwd`` (dq, dk, dv),
+``SkiparseAttention`` (a torch.autograd.Function over the last two),
+``quantize_weights`` and ``BlockFP8`` (the fp8 attention block).
 
 There is no fallback: if libskiparse.so is missing the calls raise.
 """
@@ -68,6 +76,11 @@ EXPORTED = (
     "skiparse_attn_bwd",
     "skiparse_quant_fp8_workspace_bytes",
     "skiparse_quant_fp8",
+    "skiparse_block_workspace_bytes",
+    "skiparse_block_fwd_fp8",
+    "skiparse_gemm_fp8",
+    "skiparse_rope_fp8_workspace_bytes",
+    "skiparse_rope_fp8",
     "skiparse_last_error",
 )
 
@@ -143,6 +156,16 @@ def lib():
     L.skiparse_quant_fp8.restype = ctypes.c_int
     L.skiparse_quant_fp8.argtypes = [vp, ctypes.c_int, ctypes.c_int64, vp, vp, ctypes.c_float, ctypes.c_float,
                                      vp, ctypes.c_size_t, vp]
+    L.skiparse_block_workspace_bytes.restype = ctypes.c_size_t
+    L.skiparse_block_workspace_bytes.argtypes = [P]
+    L.skiparse_block_fwd_fp8.restype = ctypes.c_int
+    L.skiparse_block_fwd_fp8.argtypes = [P, vp, vp, vp, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp]
+    L.skiparse_gemm_fp8.restype = ctypes.c_int
+    L.skiparse_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp]
+    L.skiparse_rope_fp8_workspace_bytes.restype = ctypes.c_size_t
+    L.skiparse_rope_fp8_workspace_bytes.argtypes = [P]
+    L.skiparse_rope_fp8.restype = ctypes.c_int
+    L.skiparse_rope_fp8.argtypes = [P, vp, ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.skiparse_last_error.restype = ctypes.c_char_p
     L.skiparse_last_error.argtypes = []
     if L.skiparse_abi_version() != ABI_VERSION:
@@ -258,6 +281,53 @@ def skiparse_quant_fp8(x, y, scale, fp8_max: float = 448.0, eps: float = 1e-12, 
     return y
 
 
+def skiparse_block_workspace_bytes(plan: SkiparsePlan) -> int:
+    return int(lib().skiparse_block_workspace_bytes(ctypes.byref(plan)))
+
+
+def skiparse_block_fwd_fp8(plan: SkiparsePlan, x, w_qkvo, w_scales, y, rope_theta: float = 10000.0,
+                           rope_dims=None, workspace=None, stream=None):
+    """fp8 attention block; ``workspace`` (device, >= skiparse_block_workspace_bytes,
+    256-byte aligned) is allocated with torch when None."""
+    if workspace is None:
+        import torch
+        workspace = torch.empty(skiparse_block_workspace_bytes(plan), dtype=torch.uint8, device=x.device)
+    wb = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    dims = None if rope_dims is None else (ctypes.c_int32 * 3)(*rope_dims)
+    _check(lib().skiparse_block_fwd_fp8(ctypes.byref(plan), _ptr(x), _ptr(w_qkvo), _ptr(w_scales),
+                                        float(rope_theta), dims, _ptr(y), _ptr(workspace), wb, _stream(stream)))
+    return y
+
+
+def skiparse_gemm_fp8(x, w, sx, sw, y, stream=None):
+    """y (M, N) bf16 = sx * sw * x (M, K) . w (N, K)^T on e4m3 codes (uint8
+    device tensors); sx, sw: device fp32 dequantization factors (1/scale)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError("shapes must be x (M, K), w (N, K), y (M, N)")
+    _check(lib().skiparse_gemm_fp8(_ptr(x), _ptr(w), _ptr(sx), _ptr(sw), _ptr(y), M, N, K, _stream(stream)))
+    return y
+
+
+def skiparse_rope_fp8_workspace_bytes(plan: SkiparsePlan) -> int:
+    return int(lib().skiparse_rope_fp8_workspace_bytes(ctypes.byref(plan)))
+
+
+def skiparse_rope_fp8(plan: SkiparsePlan, x, y, scale, rope_theta: float = 10000.0, rope_dims=None,
+                      workspace=None, stream=None):
+    """y = e4m3 codes of the rotated x, scale = {scale, 1/scale}; ``workspace``
+    is allocated with torch when None."""
+    if workspace is None:
+        import torch
+        workspace = torch.empty(skiparse_rope_fp8_workspace_bytes(plan), dtype=torch.uint8, device=x.device)
+    wb = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    dims = None if rope_dims is None else (ctypes.c_int32 * 3)(*rope_dims)
+    _check(lib().skiparse_rope_fp8(ctypes.byref(plan), _ptr(x), float(rope_theta), dims, _ptr(y), _ptr(scale),
+                                   _ptr(workspace), wb, _stream(stream)))
+    return y
+
+
 # ---------------------------------------------------------------------------
 # conveniences (torch allocates, the library computes)
 # ---------------------------------------------------------------------------
@@ -342,6 +412,51 @@ def attention_bwd(q, k, v, o, dout, lse, kf: int, mode: int, softmax_scale: floa
     skiparse_attn_bwd(plan, _dtype_code(q), q.contiguous(), k.contiguous(), v.contiguous(), o.contiguous(),
                       dout.contiguous(), lse, dq, dk, dv, softmax_scale)
     return dq, dk, dv
+
+
+def quantize_weights(wq, wk, wv, wo):
+    """Per-tensor e4m3 codes of four (C, C) weights (fp32 or bf16, device) in
+    one (4, C, C) uint8 tensor, and their {scale, 1/scale} as fp32 (4, 2)."""
+    import torch
+    ws = (wq, wk, wv, wo)
+    C = wq.shape[0]
+    for w in ws:
+        if tuple(w.shape) != (C, C):
+            raise ValueError("weights must all be (C, C)")
+    codes = torch.empty((4, C, C), dtype=torch.uint8, device=wq.device)
+    scales = torch.empty((4, 2), dtype=torch.float32, device=wq.device)
+    for i, w in enumerate(ws):
+        skiparse_quant_fp8(w.contiguous(), codes[i], scales[i])
+    return codes, scales
+
+
+class BlockFP8:
+    """The fp8 attention block on one device: e4m3 projections, rotary
+    embedding, Skiparse attention.  Holds a workspace sized for the largest
+    shape seen."""
+
+    def __init__(self, w_codes, w_scales, heads: int, kf: int, mode: int, rope_theta: float = 10000.0,
+                 rope_dims=None):
+        self.w_codes, self.w_scales = w_codes, w_scales
+        self.heads, self.kf, self.mode = heads, kf, mode
+        self.rope_theta, self.rope_dims = rope_theta, rope_dims
+        self._ws = None
+
+    def __call__(self, x, out=None):
+        import torch
+        if x.dim() != 5 or x.dtype != torch.bfloat16 or not x.is_contiguous():
+            raise ValueError("x must be contiguous bf16 (B, T, H, W, C)")
+        B, T, H, W, C = x.shape
+        if C % self.heads:
+            raise ValueError("C must be a multiple of heads")
+        plan = skiparse_plan_init(B, T, H, W, self.heads, C // self.heads, self.kf, self.mode)
+        need = skiparse_block_workspace_bytes(plan)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = None
+            self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        y = torch.empty_like(x) if out is None else out
+        skiparse_block_fwd_fp8(plan, x, self.w_codes, self.w_scales, y, self.rope_theta, self.rope_dims, self._ws)
+        return y
 
 
 def _autograd_function():

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libskiparse.so")
 
-SOURCES = ["api.hip", "attn_bf16.hip", "attn_bwd.hip", "attn_f32.hip", "attn_fp8.hip", "index_map.hip", "quant_fp8.hip"]
+SOURCES = ["api.hip", "attn_bf16.hip", "block_fp8.hip", "gemm_fp8.hip", "attn_bwd.hip", "attn_f32.hip", "attn_fp8.hip", "index_map.hip", "quant_fp8.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -6,7 +6,7 @@
 #include <cstring>
 #include <string>
 
-#include "internal.h"
+#include "block.h"
 
 using namespace skiparse;
 
@@ -23,6 +23,8 @@ int fail(int code, const char* fmt, ...) {
   g_err = buf;
   return code;
 }
+
+constexpr float kE4M3MaxHost = 448.0f;
 
 int ok() {
   g_err.clear();
@@ -402,6 +404,209 @@ int skiparse_quant_fp8(const void* x, skiparse_dtype x_dtype, int64_t numel, uin
   (void)hipGetLastError();
   const hipError_t e = launch_quant_fp8(x, x_dtype == SKIPARSE_BF16, numel, y, dev_scale, fp8_max, eps, workspace, stream);
   if (e != hipSuccess) return fail(SKIPARSE_EHIP, "quantization launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// fp8 attention block
+// ---------------------------------------------------------------------------
+
+namespace {
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Byte offsets of the block's scratch buffers inside the caller's workspace.
+struct BlockLayout {
+  size_t x8, qkv16, qkv8, scales, part, tab, total;
+};
+
+// Rotary geometry of a plan's (B, T, H, W, heads, d) tensor; validates theta,
+// the split and the size.
+int rope_setup(const skiparse_plan& p, float theta, const int32_t* rope_dims, RopeGeom& r) {
+  const int d = p.d;
+  if (d < 8 || (d & (d - 1)) != 0) return fail(SKIPARSE_EUNSUPPORTED, "the rotary kernels need d a power of two >= 8 (d=%d)", d);
+  if (!(theta > 0.f) || !std::isfinite(theta)) return fail(SKIPARSE_EINVAL, "rope_theta must be positive and finite");
+  int32_t dims[3];
+  if (rope_dims && (rope_dims[0] || rope_dims[1] || rope_dims[2])) {
+    for (int i = 0; i < 3; ++i) dims[i] = rope_dims[i];
+    if (dims[0] < 0 || dims[1] < 0 || dims[2] < 0 || ((dims[0] | dims[1] | dims[2]) & 1) ||
+        (int64_t)dims[0] + dims[1] + dims[2] != d)
+      return fail(SKIPARSE_EINVAL, "rope_dims (%d, %d, %d) must be even, non-negative and sum to d=%d", dims[0],
+                  dims[1], dims[2], d);
+  } else {
+    dims[1] = dims[2] = 2 * (d / 6);
+    dims[0] = d - 2 * dims[1];
+  }
+  const int64_t mc = (int64_t)p.B * p.T * p.H * p.W * p.heads * d;
+  if (mc / 8 >= (int64_t(1) << 31)) return fail(SKIPARSE_EINVAL, "B*T*H*W*heads*d / 8 must stay below 2^31");
+  r.T = p.T;
+  r.H = p.H;
+  r.W = p.W;
+  r.d = d;
+  r.dt = dims[0];
+  r.dh = dims[1];
+  r.dw = dims[2];
+  r.tab_h = p.T * (dims[0] / 2);
+  r.tab_w = r.tab_h + p.H * (dims[1] / 2);
+  r.tab_len = r.tab_w + p.W * (dims[2] / 2);
+  r.nvec = (uint32_t)(mc / 8);
+  r.div_cv = make_fastdiv((uint32_t)((int64_t)p.heads * d / 8));
+  r.div_w = make_fastdiv((uint32_t)p.W);
+  r.div_h = make_fastdiv((uint32_t)p.H);
+  r.div_t = make_fastdiv((uint32_t)p.T);
+  return SKIPARSE_OK;
+}
+
+size_t rope_table_bytes(const skiparse_plan& p) {
+  return round256((size_t)(p.T + p.H + p.W) * (p.d / 2) * sizeof(float2));
+}
+
+size_t rope_part_bytes(const skiparse_plan& p) {
+  const size_t nvec = (size_t)p.B * p.T * p.H * p.W * p.heads * p.d / 8;
+  return round256(rope_partials_bytes((uint32_t)(nvec < (size_t(1) << 31) ? nvec : 1)));
+}
+
+BlockLayout block_layout(const skiparse_plan& p) {
+  const size_t mc = (size_t)p.B * p.T * p.H * p.W * p.heads * p.d;
+  const size_t nvec = mc / 8;
+  size_t part = quant_workspace_bytes((int64_t)mc);
+  const size_t rp = rope_partials_bytes((uint32_t)(nvec < (size_t(1) << 31) ? nvec : 1));
+  if (rp > part) part = rp;
+  BlockLayout L;
+  size_t at = 0;
+  L.x8 = at, at += round256(mc);                 // x codes, later O codes
+  L.qkv16 = at, at += round256(3 * mc * 2);      // Q, K, V projections (bf16), later O (bf16) over Q
+  L.qkv8 = at, at += round256(3 * mc);           // Q, K, V codes
+  L.scales = at, at += 256;                      // {s, 1/s} of x, Q, K, V, O
+  L.part = at, at += round256(part);
+  L.tab = at, at += rope_table_bytes(p);
+  L.total = at;
+  return L;
+}
+
+}  // namespace
+
+size_t skiparse_block_workspace_bytes(const skiparse_plan* plan) {
+  if (check_plan(plan)) return 0;
+  return block_layout(*plan).total;
+}
+
+int skiparse_block_fwd_fp8(const skiparse_plan* plan, const void* x, const uint8_t* w_qkvo, const float* dev_w_scales,
+                           float rope_theta, const int32_t* rope_dims, void* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (int e = check_plan(plan)) return e;
+  const int d = plan->d;
+  if (d != 128) return fail(SKIPARSE_EUNSUPPORTED, "the fp8 block is built for d=128 only (d=%d)", d);
+  if (!x || !w_qkvo || !dev_w_scales || !y) return fail(SKIPARSE_EINVAL, "x, w_qkvo, dev_w_scales and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(w_qkvo) || !aligned16(y))
+    return fail(SKIPARSE_EINVAL, "x, w_qkvo and y must be 16-byte aligned");
+  if (((uintptr_t)dev_w_scales & 3u) != 0) return fail(SKIPARSE_EINVAL, "dev_w_scales must be 4-byte aligned");
+  RopeGeom r;
+  if (int e = rope_setup(*plan, rope_theta, rope_dims, r)) return e;
+  const int64_t C = (int64_t)plan->heads * d;
+  const int64_t M = (int64_t)plan->B * plan->T * plan->H * plan->W;
+  const int64_t mc = M * C;
+  if (C > 65536) return fail(SKIPARSE_EUNSUPPORTED, "heads*d = %lld is above 65536", (long long)C);
+  if (M >= (int64_t(1) << 31)) return fail(SKIPARSE_EINVAL, "B*T*H*W must stay below 2^31");
+  const BlockLayout L = block_layout(*plan);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(SKIPARSE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? workspace_bytes : 0);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(SKIPARSE_EINVAL, "workspace must be 256-byte aligned");
+  const size_t wb = (size_t)(4 * C * C);
+  if (overlap(y, mc * 2, x, mc * 2) || overlap(y, mc * 2, w_qkvo, wb) || overlap(workspace, L.total, x, mc * 2) ||
+      overlap(workspace, L.total, y, mc * 2) || overlap(workspace, L.total, w_qkvo, wb) ||
+      overlap(workspace, L.total, dev_w_scales, 32))
+    return fail(SKIPARSE_EINVAL, "y and the workspace must not overlap each other or the inputs");
+
+  char* ws = (char*)workspace;
+  uint8_t* x8 = (uint8_t*)(ws + L.x8);
+  char* b16 = ws + L.qkv16;
+  uint8_t* c8 = (uint8_t*)(ws + L.qkv8);
+  float* sc = (float*)(ws + L.scales);
+  float* part = (float*)(ws + L.part);
+  float2* tab = (float2*)(ws + L.tab);
+
+  AttnArgs a;
+  int32_t all = 0;
+  if (int e = training_args(plan, SKIPARSE_BF16, 0.f, 0, all, a)) return e;
+  a.q = c8;
+  a.k = c8 + mc;
+  a.v = c8 + 2 * mc;
+  a.o = b16;                 // O (bf16) over the Q projection, dead by then
+  a.descale = sc + 2;        // {s_q, 1/s_q, s_k, 1/s_k, s_v, 1/s_v}
+
+  (void)hipGetLastError();
+  auto hip_fail = [&](hipError_t e, const char* what) {
+    return fail(SKIPARSE_EHIP, "%s failed: %s", what, hipGetErrorString(e));
+  };
+  hipError_t e = launch_quant_fp8(x, 1, mc, x8, sc, kE4M3MaxHost, 1e-12f, part, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantization of x");
+  for (int i = 0; i < 3; ++i)
+    if ((e = launch_gemm_fp8_bf16(x8, w_qkvo + i * C * C, sc + 1, dev_w_scales + 2 * i + 1, b16 + i * mc * 2, M,
+                                  (int)C, (int)C, stream)) != hipSuccess)
+      return hip_fail(e, "projection");
+  if ((e = launch_rope_table(r, rope_theta, tab, stream)) != hipSuccess) return hip_fail(e, "rotary table");
+  for (int i = 0; i < 2; ++i)
+    if ((e = launch_rope_quant(r, tab, b16 + i * mc * 2, c8 + i * mc, sc + 2 + 2 * i, part, stream)) != hipSuccess)
+      return hip_fail(e, "rotary embedding");
+  if ((e = launch_quant_fp8(b16 + 2 * mc * 2, 1, mc, c8 + 2 * mc, sc + 6, kE4M3MaxHost, 1e-12f, part, stream)) != hipSuccess)
+    return hip_fail(e, "quantization of V");
+  if ((e = launch_attn_fp8(a, plan->B, d, stream)) != hipSuccess) return hip_fail(e, "attention");
+  if ((e = launch_quant_fp8(b16, 1, mc, x8, sc + 8, kE4M3MaxHost, 1e-12f, part, stream)) != hipSuccess)
+    return hip_fail(e, "quantization of O");
+  if ((e = launch_gemm_fp8_bf16(x8, w_qkvo + 3 * C * C, sc + 9, dev_w_scales + 7, y, M, (int)C, (int)C, stream)) !=
+      hipSuccess)
+    return hip_fail(e, "output projection");
+  return ok();
+}
+
+int skiparse_gemm_fp8(const uint8_t* x, const uint8_t* w, const float* dev_sx, const float* dev_sw, void* y,
+                      int64_t M, int32_t N, int32_t K, hipStream_t stream) {
+  if (M < 1 || M >= (int64_t(1) << 31)) return fail(SKIPARSE_EINVAL, "M=%lld outside [1, 2^31)", (long long)M);
+  if (N < 128 || K < 128 || N % 128 || K % 128 || N > 65536 || K > 65536)
+    return fail(SKIPARSE_EUNSUPPORTED, "N=%d and K=%d must be multiples of 128 in [128, 65536]", N, K);
+  if (((M + 127) / 128) * (N / 128) >= (int64_t(1) << 31)) return fail(SKIPARSE_EINVAL, "too many tiles");
+  if (!x || !w || !dev_sx || !dev_sw || !y) return fail(SKIPARSE_EINVAL, "x, w, dev_sx, dev_sw and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(w) || ((uintptr_t)y & 7u) != 0 || ((uintptr_t)dev_sx & 3u) != 0 ||
+      ((uintptr_t)dev_sw & 3u) != 0)
+    return fail(SKIPARSE_EINVAL, "x and w must be 16-byte aligned, y 8-byte, dev_sx and dev_sw 4-byte");
+  const size_t yb = (size_t)M * N * 2;
+  if (overlap(y, yb, x, (size_t)M * K) || overlap(y, yb, w, (size_t)N * K) || overlap(y, yb, dev_sx, 4) ||
+      overlap(y, yb, dev_sw, 4))
+    return fail(SKIPARSE_EINVAL, "y must not overlap the inputs");
+  (void)hipGetLastError();
+  const hipError_t e = launch_gemm_fp8_bf16(x, w, dev_sx, dev_sw, y, M, N, K, stream);
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "GEMM launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t skiparse_rope_fp8_workspace_bytes(const skiparse_plan* plan) {
+  if (check_plan(plan)) return 0;
+  return rope_table_bytes(*plan) + rope_part_bytes(*plan);
+}
+
+int skiparse_rope_fp8(const skiparse_plan* plan, const void* x, float rope_theta, const int32_t* rope_dims,
+                      uint8_t* y, float* dev_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int e = check_plan(plan)) return e;
+  RopeGeom r;
+  if (int e = rope_setup(*plan, rope_theta, rope_dims, r)) return e;
+  if (!x || !y || !dev_scale) return fail(SKIPARSE_EINVAL, "x, y and dev_scale must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)dev_scale & 3u) != 0)
+    return fail(SKIPARSE_EINVAL, "x and y must be 16-byte aligned, dev_scale 4-byte aligned");
+  const size_t need = rope_table_bytes(*plan) + rope_part_bytes(*plan);
+  if (!workspace || workspace_bytes < need)
+    return fail(SKIPARSE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (((uintptr_t)workspace & 15u) != 0) return fail(SKIPARSE_EINVAL, "workspace must be 16-byte aligned");
+  const size_t n = (size_t)r.nvec * 8;
+  if (overlap(y, n, x, 2 * n) || overlap(workspace, need, x, 2 * n) || overlap(workspace, need, y, n) ||
+      overlap(dev_scale, 8, x, 2 * n) || overlap(dev_scale, 8, y, n) || overlap(dev_scale, 8, workspace, need))
+    return fail(SKIPARSE_EINVAL, "x, y, dev_scale and the workspace must not overlap");
+  float2* tab = (float2*)workspace;
+  float* part = (float*)((char*)workspace + rope_table_bytes(*plan));
+  (void)hipGetLastError();
+  hipError_t e = launch_rope_table(r, rope_theta, tab, stream);
+  if (e == hipSuccess) e = launch_rope_quant(r, tab, x, y, dev_scale, part, stream);
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "rotary embedding launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -10,33 +10,14 @@
 //   3. y = e4m3(x * scale): the fp32 product is clamped to +-448 and
 //      converted by v_cvt_pk_fp8_f32 (round to nearest even), which equals
 //      round-to-nearest-even with saturation.
-#include "internal.h"
+#include "fp8_codec.h"
+#include "block.h"
 
 namespace skiparse {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kQuantThreads;
 constexpr int kMaxBlocks = 2048;
-constexpr float kE4M3Max = 448.0f;
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ float block_max(float v) {
-  __shared__ float part[kThreads / 64];
-  v = wave_max(v);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = part[0];
-#pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, part[i]);
-  return r;
-}
 
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const void* __restrict__ x, int64_t numel,
@@ -79,13 +60,6 @@ __global__ void __launch_bounds__(kThreads) scale_kernel(const float* __restrict
     scale[0] = s;
     scale[1] = 1.0f / s;
   }
-}
-
-__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d, float s) {
-  auto sat = [](float v) { return fminf(fmaxf(v, -kE4M3Max), kE4M3Max); };
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a * s), sat(b * s), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c * s), sat(d * s), w, true);
-  return (uint32_t)w;
 }
 
 template <bool BF16>
@@ -133,6 +107,12 @@ int blocks_for(int64_t numel) {
 }  // namespace
 
 size_t quant_workspace_bytes(int64_t numel) { return (size_t)blocks_for(numel) * sizeof(float); }
+
+hipError_t launch_fp8_scale(const float* part, int nparts, float fp8_max, float eps, float* scale,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(scale_kernel, dim3(1), dim3(kThreads), 0, stream, part, nparts, fp8_max, eps, scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_fp8(const void* x, int x_is_bf16, int64_t numel, uint8_t* y, float* scale,
                             float fp8_max, float eps, void* ws, hipStream_t stream) {

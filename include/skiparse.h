@@ -229,6 +229,96 @@ int skiparse_quant_fp8(const void* x, skiparse_dtype x_dtype, int64_t numel, uin
                        float* dev_scale, float fp8_max, float eps,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * One attention block of the 8-bit video DiT around the sparse attention.
+ * The DiT trains and runs with per-tensor 8-bit quantization,
+ * scale = fp8_max / (amax + eps) (OSP-Next summary, 方法步骤详情 method steps;
+ * 核心方法 core method: the sparse layers between full-attention ones); the
+ * pages name the projections and the rotary position embedding around the
+ * attention without defining them, so the block takes their plainest form:
+ *     x^ = q8(x)
+ *     Q = x^ Wq^T,  K = x^ Wk^T,  V = x^ Wv^T        (e4m3 x e4m3, fp32 accumulation)
+ *     Q, K = rope(Q), rope(K)
+ *     O = skiparse_attn_fwd(q8(Q), q8(K), q8(V))      (SKIPARSE_FP8_E4M3, all subsequences)
+ *     y = q8(O) Wo^T                                   (skiparse_gemm_fp8)
+ * q8 is skiparse_quant_fp8 with fp8_max 448, eps 1e-12, one scale per
+ * tensor.  rope turns, inside head dimension part a in {t, h, w} of size
+ * d_a, the pair (x_2i, x_2i+1) (i counted from the part's start) by the angle
+ * pos_a * theta^(-2i / d_a), pos_a the token's frame, row or column; the parts
+ * follow each other in the order t, h, w.  The projections' bf16 outputs Q,
+ * K, V and the attention's bf16 output O are what gets quantized.
+ */
+
+/* Workspace bytes of skiparse_block_fwd_fp8 for this plan (about
+ * 10 * B*T*H*W*heads*d); 0 for an invalid plan. */
+size_t skiparse_block_workspace_bytes(const skiparse_plan* plan);
+
+/*
+ * Forward pass of the block on the stream.
+ *   plan          B, T, H, W, heads, d = 128, k and mode of the attention;
+ *                 C = heads * d channels per token
+ *   x             device bf16 (B, T, H, W, C), 16-byte aligned
+ *   w_qkvo        device e4m3 codes of Wq, Wk, Wv, Wo one after the other,
+ *                 each (C, C) row-major in (out, in) layout (a linear
+ *                 layer's weight), 16-byte aligned
+ *   dev_w_scales  device fp32 (4, 2): {scale, 1/scale} of each weight as
+ *                 skiparse_quant_fp8 writes them (weight = code / scale)
+ *   rope_theta    base of the rotary angles (10000 in the usual form), > 0
+ *   rope_dims     {d_t, d_h, d_w}: even, summing to d; NULL or {0, 0, 0} for
+ *                 d_h = d_w = 2 * (d / 6), d_t = d - d_h - d_w (44, 42, 42)
+ *   y             device bf16 (B, T, H, W, C), 16-byte aligned
+ *   workspace     device, >= skiparse_block_workspace_bytes(plan) bytes,
+ *                 256-byte aligned; scratch, overwritten
+ * y and the workspace must not overlap each other or any input.  Inputs must
+ * be finite.  Errors: SKIPARSE_EINVAL, SKIPARSE_EUNSUPPORTED (d != 128),
+ * SKIPARSE_EWORKSPACE, SKIPARSE_EHIP (launches before a failing one stay
+ * enqueued).
+ */
+int skiparse_block_fwd_fp8(const skiparse_plan* plan, const void* x, const uint8_t* w_qkvo,
+                           const float* dev_w_scales, float rope_theta, const int32_t* rope_dims, void* y,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The block's projection on its own: an e4m3 GEMM with fp32 accumulation and
+ * bf16 output (round to nearest even),
+ *     y[m][n] = (*dev_sx) * (*dev_sw) * sum_k x[m][k] * w[n][k],
+ * x and w holding e4m3 codes; dev_sx and dev_sw are the dequantization
+ * factors 1/scale of x and w (the second float skiparse_quant_fp8 writes).
+ *   x        device (M, K) row-major, 16-byte aligned
+ *   w        device (N, K) row-major ((out, in), a linear layer's weight),
+ *            16-byte aligned
+ *   y        device bf16 (M, N) row-major, 8-byte aligned; must not overlap
+ *            the inputs
+ *   M        1 <= M < 2^31;  N, K: multiples of 128 in [128, 65536]
+ * Errors: SKIPARSE_EINVAL, SKIPARSE_EUNSUPPORTED (N or K not a multiple of
+ * 128), SKIPARSE_EHIP.
+ */
+int skiparse_gemm_fp8(const uint8_t* x, const uint8_t* w, const float* dev_sx, const float* dev_sw, void* y,
+                      int64_t M, int32_t N, int32_t K, hipStream_t stream);
+
+/* Workspace bytes of skiparse_rope_fp8 for this plan; 0 for an invalid plan. */
+size_t skiparse_rope_fp8_workspace_bytes(const skiparse_plan* plan);
+
+/*
+ * The block's rotary embedding and quantization on their own:
+ * y = q8(rope(x)) with the rotation and q8 of skiparse_block_fwd_fp8.  The
+ * rotation runs in fp32 from cos/sin rounded to fp32 from float64; the scale
+ * comes from max |rope(x)| over the whole tensor.
+ *   plan         B, T, H, W, heads and d of x (d a power of two >= 8; k and
+ *                mode unused)
+ *   x            device bf16 (B, T, H, W, heads, d), 16-byte aligned
+ *   rope_theta, rope_dims   as for skiparse_block_fwd_fp8
+ *   y            device, B*T*H*W*heads*d e4m3 codes, 16-byte aligned
+ *   dev_scale    device, 2 fp32: {scale, 1/scale}
+ *   workspace    device, >= skiparse_rope_fp8_workspace_bytes(plan) bytes,
+ *                16-byte aligned; scratch, overwritten
+ * Errors: SKIPARSE_EINVAL, SKIPARSE_EUNSUPPORTED, SKIPARSE_EWORKSPACE,
+ * SKIPARSE_EHIP.
+ */
+int skiparse_rope_fp8(const skiparse_plan* plan, const void* x, float rope_theta, const int32_t* rope_dims,
+                      uint8_t* y, float* dev_scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 /* Description of the last error on the calling thread ("" if none); valid
  * until the next library call on that thread. */
 const char* skiparse_last_error(void);

@@ -255,3 +255,67 @@ def test_fastdiv_exact(tmp_path):
     subprocess.run(["g++", "-O2", "-std=c++17", "-I", inc, str(src), "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "OK", r.stdout
+
+
+def test_rope_argument_errors():
+    import ctypes
+    L = sk.lib()
+    p = sk.skiparse_plan_init(1, 2, 4, 6, 2, 128, 2, 0)
+    need = sk.skiparse_rope_fp8_workspace_bytes(p)
+    assert need > 0
+    dims = lambda *d: (ctypes.c_int32 * 3)(*d)
+    call = lambda plan=p, x=0x10000, th=10000.0, dm=None, y=0x100000, sc=0x200000, ws=0x300000, wb=need: \
+        L.skiparse_rope_fp8(ctypes.byref(plan), x, th, dm, y, sc, ws, wb, None)
+    assert call(wb=need - 1) == sk.EWORKSPACE
+    assert call(ws=None) == sk.EWORKSPACE
+    assert call(th=0.0) == sk.EINVAL
+    assert call(th=float("inf")) == sk.EINVAL
+    assert call(dm=dims(44, 42, 40)) == sk.EINVAL        # does not sum to d
+    assert call(dm=dims(43, 43, 42)) == sk.EINVAL        # odd parts
+    assert call(dm=dims(-2, 66, 64)) == sk.EINVAL
+    assert call(x=0x10008) == sk.EINVAL                  # misaligned
+    assert call(y=0x10000 + 64) == sk.EINVAL             # y inside x
+    assert call(x=None) == sk.EINVAL
+    p96 = sk.skiparse_plan_init(1, 2, 4, 6, 2, 96, 2, 0)
+    assert L.skiparse_rope_fp8(ctypes.byref(p96), 0x10000, 1e4, None, 0x100000, 0x200000, 0x300000, 1 << 20, None) \
+        == sk.EUNSUPPORTED
+    assert sk.skiparse_last_error()
+
+
+def test_block_argument_errors():
+    import ctypes
+    L = sk.lib()
+    p = sk.skiparse_plan_init(1, 2, 4, 6, 2, 128, 2, 0)
+    need = sk.skiparse_block_workspace_bytes(p)
+    mc = 2 * 4 * 6 * 256
+    assert need >= 10 * mc
+    bad = sk.SkiparsePlan()
+    assert sk.skiparse_block_workspace_bytes(bad) == 0
+    call = lambda plan=p, x=0x10000, wq=0x4000000, sc=0x8000000, th=1e4, y=0x100000, ws=0x10000000, wb=need: \
+        L.skiparse_block_fwd_fp8(ctypes.byref(plan), x, wq, sc, th, None, y, ws, wb, None)
+    assert call(wb=need - 1) == sk.EWORKSPACE
+    assert call(ws=None) == sk.EWORKSPACE
+    assert call(ws=0x10000000 + 16) == sk.EINVAL           # not 256-byte aligned
+    assert call(x=None) == sk.EINVAL
+    assert call(th=-1.0) == sk.EINVAL
+    assert call(y=0x10000 + 1024) == sk.EINVAL             # y overlaps x
+    assert call(ws=0x10000 - 256) == sk.EINVAL             # workspace overlaps x
+    p64 = sk.skiparse_plan_init(1, 2, 4, 6, 2, 64, 2, 0)
+    assert call(plan=p64) == sk.EUNSUPPORTED
+
+
+def test_gemm_argument_errors():
+    L = sk.lib()
+    call = lambda x=0x10000, w=0x100000, sx=0x200000, sw=0x200010, y=0x1000000, M=300, N=256, K=384: \
+        L.skiparse_gemm_fp8(x, w, sx, sw, y, M, N, K, None)
+    assert call(M=0) == sk.EINVAL
+    assert call(M=1 << 31) == sk.EINVAL
+    assert call(N=200) == sk.EUNSUPPORTED
+    assert call(K=100) == sk.EUNSUPPORTED
+    assert call(N=0) == sk.EUNSUPPORTED
+    assert call(x=0x10008) == sk.EINVAL
+    assert call(y=0x1000004) == sk.EINVAL
+    assert call(sx=0x200002) == sk.EINVAL
+    assert call(w=None) == sk.EINVAL
+    assert call(y=0x10000 + 64) == sk.EINVAL               # y overlaps x
+    assert sk.skiparse_last_error()

@@ -1,0 +1,95 @@
+"""GPU parity of the block's e4m3 projection GEMM (skiparse_gemm_fp8) against
+its definition y[m][n] = sx * sw * sum_k x[m][k] w[n][k] evaluated in float64
+on the decoded codes.
+
+Bar, per element: a product of two e4m3 values is exact in fp32 and K of them
+are summed in fp32, so the accumulated sum is within gamma_K * sum_k |x w| of
+the exact one (gamma_K = K u / (1 - K u), u = 2^-24); the scale product and
+the multiply add two fp32 roundings, and the bf16 conversion (round to
+nearest even, 8 significant bits) at most 2^-8 relative.  The test allows
+|y - ref| <= 2^-8 |ref| + 2 * (gamma_K + 2u) * sx * sw * sum_k |x w|, with a
+slack factor of 2 on the fp32 part.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fixed_pattern_sparse_amd as sk
+import workloads as wl
+from oracle import fp8_ref as f8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+U = 2.0 ** -24
+
+
+def codes(shape, seed, tid, std=1.0):
+    """e4m3 codes of seeded normal values through the oracle's codec (per
+    tensor scale), and the scale it chose."""
+    v = wl.normal_tensor(shape, seed, tid) * np.float32(std)
+    c, s, _ = f8.quantize_per_tensor(v.reshape(-1))
+    return c.reshape(shape), s
+
+
+def check(y_dev, xc, wc, sx, sw, rows=None):
+    """Compare rows of y_dev (float64) with the definition on those rows."""
+    xv = f8.e4m3_decode(xc if rows is None else xc[rows]).astype(np.float64)
+    wv = f8.e4m3_decode(wc).astype(np.float64)
+    s = float(np.float32(sx)) * float(np.float32(sw))
+    ref = s * (xv @ wv.T)
+    mag = s * (np.abs(xv) @ np.abs(wv).T)
+    K = xc.shape[1]
+    gamma = K * U / (1 - K * U)
+    bound = 2.0 ** -8 * np.abs(ref) + 2 * (gamma + 2 * U) * mag
+    got = y_dev if rows is None else y_dev[rows]
+    assert np.all(np.isfinite(got))
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{bad.sum()} elements out of bound; worst excess {np.max(np.abs(got - ref) - bound)}"
+
+
+def run(xc, wc, sx, sw):
+    M, K = xc.shape
+    N = wc.shape[0]
+    xd = torch.from_numpy(xc).to(DEV)
+    wd = torch.from_numpy(wc).to(DEV)
+    sc = torch.tensor([sx, sw], dtype=torch.float32, device=DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    sk.skiparse_gemm_fp8(xd, wd, sc[0:1], sc[1:2], y)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 256, 384), (257, 384, 128), (128, 128, 1024),
+                                   (1000, 3072, 256), (4097, 512, 640)])
+def test_gemm_small(M, N, K):
+    xc, xs = codes((M, K), 901, 0)
+    wc, ws = codes((N, K), 901, 1, 1.0 / np.sqrt(K))
+    y = run(xc, wc, 1.0 / xs, 1.0 / ws)
+    check(y, xc, wc, 1.0 / xs, 1.0 / ws)
+
+
+def test_gemm_extreme_codes():
+    """Largest codes (+-448) in every position: the fp32 sums reach
+    K * 448^2 without overflow and the scale brings them back."""
+    M, N, K = 130, 256, 256
+    xc = np.full((M, K), 0x7E, np.uint8)          # +448
+    xc[::3] = 0xFE                                # -448
+    wc = np.full((N, K), 0x7E, np.uint8)
+    y = run(xc, wc, 2.0 ** -10, 2.0 ** -10)
+    check(y, xc, wc, 2.0 ** -10, 2.0 ** -10)
+
+
+def test_gemm_projection_shape_sampled():
+    """The block's projection at 720P-5s: M = 21 * 45 * 80 tokens,
+    N = K = 24 heads * 128; sampled rows, the last tile's rows included."""
+    w = wl.WORKLOADS["720p_5s"]
+    B, T, H, W, heads, d = w.shape
+    M, C = B * T * H * W, heads * d
+    xc, xs = codes((M, C), 902, 0)
+    wc, ws = codes((C, C), 902, 1, 1.0 / np.sqrt(C))
+    y = run(xc, wc, 1.0 / xs, 1.0 / ws)
+    rng = np.random.Generator(np.random.PCG64(903))
+    rows = np.unique(np.concatenate([rng.choice(M, 40, replace=False), np.arange(M - 100, M), np.arange(0, 4)]))
+    check(y, xc, wc, 1.0 / xs, 1.0 / ws, rows)
