@@ -10,7 +10,8 @@ same subsequence) pairs, ms per step, the roofline of the attention kernel
 (average launch duration from HIP events on the launch stream), the oracle's
 CPU baseline on a bounded sample, and extras: ms per layer, the same kernel at
 k = 1 (full attention), the fp8 path, a training step (forward with the
-log-sum-exp, backward) and Skiparse-1D.
+log-sum-exp, backward), Skiparse-1D, and the fp8 block's projection GEMM and
+rotary quantizer.
 """
 
 from __future__ import annotations
@@ -295,6 +296,75 @@ def main():
             one_d[name] = {"ms": round(ms, 3), "tflops": round(pl.flops / (ms * 1e-3) / 1e12, 2), "pairs": int(pl.pairs)}
         extras["skiparse_1d_bf16"] = one_d
         del o1d
+        # pieces of the fp8 attention block at C = heads * d channels: the
+        # e4m3 projection GEMM (2 * tokens * C * C FLOPs) and the rotary
+        # embedding fused with per-tensor quantization (reads bf16 twice,
+        # writes e4m3 once: 5 bytes per element)
+        C = nh * d
+        M = B * T * H * W
+        xq = sk.quantize_fp8(q.reshape(M, C))[0]
+        wv = torch.from_numpy(wl.normal_tensor((C, C), w.seed, 5) * np.float32(1.0 / np.sqrt(C))).cuda()
+        wq, wsc = sk.quantize_fp8(wv)
+        del wv
+        ysc = torch.ones(2, dtype=torch.float32, device="cuda")
+        yg = torch.empty((M, C), dtype=torch.bfloat16, device="cuda")
+        sk.skiparse_gemm_fp8(xq, wq, ysc[0:1], wsc[1:2], yg, stream=stream)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(5):
+            sk.skiparse_gemm_fp8(xq, wq, ysc[0:1], wsc[1:2], yg, stream=stream)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        gms = e[0].elapsed_time(e[1]) / 5
+        gfl = 2.0 * M * C * C
+        block = {"projection_gemm": {"M": M, "N": C, "K": C, "ms": round(gms, 3),
+                                     "tflops": round(gfl / (gms * 1e-3) / 1e12, 1),
+                                     "frac_fp8_peak": round(gfl / (gms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4)}}
+        del xq, wq, yg
+        pl = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, sk.MODE_TOKEN)
+        codes_r = torch.empty(q.shape, dtype=torch.uint8, device="cuda")
+        rsc = torch.empty(2, dtype=torch.float32, device="cuda")
+        rws = torch.empty(sk.skiparse_rope_fp8_workspace_bytes(pl), dtype=torch.uint8, device="cuda")
+        sk.skiparse_rope_fp8(pl, q, codes_r, rsc, workspace=rws, stream=stream)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(5):
+            sk.skiparse_rope_fp8(pl, q, codes_r, rsc, workspace=rws, stream=stream)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        rms_ = e[0].elapsed_time(e[1]) / 5
+        rbytes = q.numel() * 5
+        block["rope_quant"] = {"ms": round(rms_, 3), "GBps": round(rbytes / (rms_ * 1e-3) / 1e9, 1),
+                               "frac_hbm_peak": round(rbytes / (rms_ * 1e-3) / 1e9 / HBM_GBS, 4)}
+        del codes_r, rws
+        # the whole fp8 block at the 480p workload shape (21 x 32 x 52 tokens,
+        # 12 heads, C = 1536): projections, rotary quantizer, attention
+        w4 = wl.WORKLOADS["480p"]
+        B4, T4, H4, W4, nh4, d4 = w4.shape
+        C4, M4 = nh4 * d4, B4 * T4 * H4 * W4
+        x4 = torch.from_numpy(wl.normal_tensor((B4, T4, H4, W4, C4), w4.seed, 4)).to(torch.bfloat16).cuda()
+        wts = [torch.from_numpy(wl.normal_tensor((C4, C4), w4.seed, 5 + i) * np.float32(1.0 / np.sqrt(C4))).cuda()
+               for i in range(4)]
+        w_codes, w_scales = sk.quantize_weights(*wts)
+        del wts
+        for mode, name in ((sk.MODE_TOKEN, "token"), (sk.MODE_GROUP, "group")):
+            pl = sk.skiparse_plan_init(B4, T4, H4, W4, nh4, d4, w4.k, mode)
+            bf = sk.BlockFP8(w_codes, w_scales, nh4, w4.k, mode)
+            y4 = bf(x4)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            for _ in range(5):
+                bf(x4, out=y4)
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            ms = e[0].elapsed_time(e[1]) / 5
+            flops = pl.flops + 4 * 2 * M4 * C4 * C4
+            block[f"block_480p_{name}"] = {"ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                                           "attention_tflop": round(pl.flops / 1e12, 3),
+                                           "projection_tflop": round(4 * 2 * M4 * C4 * C4 / 1e12, 3)}
+            del y4, bf
+        extras["block_fp8"] = block
+        del x4, w_codes, w_scales
     result["extras"] = extras
 
     if not args.no_cpu_baseline:

@@ -5,15 +5,19 @@
 // the B operand directly: each lane then holds 4 consecutive outputs of one
 // row of Y, stored as one 8-byte write.
 //
-// Work-group: 256 threads (4 waves as 2 x 2), tile 128 (n) x 128 (m); a wave
-// owns 64 x 64 as 2 x 2 blocks of v_mfma_scale_f32_32x32x64_f8f6f4.  K advances
-// 128 bytes per step through double-buffered LDS (16 KB per operand and
-// buffer), filled from registers loaded one step ahead; 16-byte chunks are
-// XOR-swizzled by row so 32 lanes reading one chunk column of 32 rows spread
-// over all banks.  N and K are multiples of 128; rows of X past M are clamped
-// on load and masked on store.  Tiles are handed out XCD by XCD (work-groups
-// are dispatched to the 8 XCDs round-robin), so the tiles that share rows of X
-// run on one XCD and share its L2.
+// A work-group computes a TN (W rows) x TM (X rows) tile; each wave owns
+// WTN x WTM of it as (WTN/32) x (WTM/32) blocks of
+// v_mfma_scale_f32_32x32x64_f8f6f4.  K advances 128 bytes per step through
+// double-buffered LDS filled from registers loaded one step ahead; 16-byte
+// chunks are XOR-swizzled by row so 32 lanes reading one chunk column of 32
+// rows spread over all banks.  Rows of X past M are clamped on load and masked
+// on store.  Tiles are handed out XCD by XCD (work-groups are dispatched to the
+// 8 XCDs round-robin), so the tiles that share rows of X run on one XCD and
+// share its L2.
+//
+// Two shapes: 256 x 256 tiles with 8 waves of 128 x 64 (arithmetic intensity
+// 256 FLOP per byte of operand traffic) when N is a multiple of 256, else
+// 128 x 128 with 4 waves of 64 x 64.
 #include "block.h"
 
 namespace skiparse {
@@ -23,112 +27,132 @@ typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kTN = 128;     // W rows (output columns) per tile
-constexpr int kTM = 128;     // X rows (output rows) per tile
 constexpr int kTK = 128;     // bytes of K per step
-constexpr int kTileB = kTN * kTK;   // 16 KB per operand tile (kTN == kTM)
 constexpr int kXcd = 8;
 
 __device__ __forceinline__ int chunk_addr(int row, int chunk) { return row * kTK + ((chunk ^ (row & 7)) << 4); }
 
-__global__ void __launch_bounds__(kThreads) gemm_fp8_bf16_kernel(const uint8_t* __restrict__ x,
-                                                                 const uint8_t* __restrict__ w,
-                                                                 const float* __restrict__ sx,
-                                                                 const float* __restrict__ sw,
-                                                                 __bf16* __restrict__ y, int M, int N, int K,
-                                                                 int tiles_n, int total) {
-  __shared__ __attribute__((aligned(16))) char lds[4 * kTileB];   // W0 W1 X0 X1
+template <int TN, int TM, int WTN, int WTM>
+struct GemmCfg {
+  static constexpr int kWavesN = TN / WTN, kWavesM = TM / WTM;
+  static constexpr int kWaves = kWavesN * kWavesM;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBN = WTN / 32, kBM = WTM / 32;         // MFMA blocks per wave
+  static constexpr int kLW = TN * (kTK / 16) / kThreads;       // 16-byte W chunks per thread and step
+  static constexpr int kLX = TM * (kTK / 16) / kThreads;
+  static constexpr int kRowsPerPass = kThreads / (kTK / 16);   // rows one pass of the loader covers
+  static constexpr int kTileW = TN * kTK, kTileX = TM * kTK;
+  static constexpr int kLds = 2 * (kTileW + kTileX);
+  static_assert(kLW * kThreads == TN * (kTK / 16) && kLX * kThreads == TM * (kTK / 16), "loader split");
+  static_assert(kRowsPerPass % 8 == 0, "rows of one chunk slot share the swizzle");
+};
+
+template <int TN, int TM, int WTN, int WTM>
+__global__ void __launch_bounds__(64 * (TN / WTN) * (TM / WTM))
+gemm_fp8_bf16_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const float* __restrict__ sx,
+                     const float* __restrict__ sw, __bf16* __restrict__ y, int M, int N, int K, int tiles_n,
+                     int total) {
+  using Cfg = GemmCfg<TN, TM, WTN, WTM>;
+  constexpr int kBN = Cfg::kBN, kBM = Cfg::kBM, kLW = Cfg::kLW, kLX = Cfg::kLX, kRP = Cfg::kRowsPerPass;
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::kLds];   // W0 W1 X0 X1
+  char* const ldsW = lds;
+  char* const ldsX = lds + 2 * Cfg::kTileW;
 
   // XCD-major tile order: XCD c runs logical tiles [start(c), start(c) + count(c)).
   const int bid = blockIdx.x;
   const int q = total / kXcd, r = total % kXcd;
   const int c = bid % kXcd;
   const int tile = c * q + (c < r ? c : r) + bid / kXcd;
-  const int n0 = (tile % tiles_n) * kTN;
-  const int m0 = (tile / tiles_n) * kTM;
+  const int n0 = (tile % tiles_n) * TN;
+  const int m0 = (tile / tiles_n) * TM;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
-  const int wn = (wave & 1) * 64;   // wave's W rows within the tile
-  const int wm = (wave >> 1) * 64;  // wave's X rows within the tile
+  const int wn = (wave % Cfg::kWavesN) * WTN;   // wave's W rows within the tile
+  const int wm = (wave / Cfg::kWavesN) * WTM;   // wave's X rows within the tile
 
-  // loader: chunk i = tid + 256 * s (s < 4) is row i / 8 = tid / 8 + 32 s,
-  // 16-byte slot i % 8 = tid % 8; X rows past M are clamped.
+  // loader: pass s < 4 covers rows tid / 8 + kRP * s, 16-byte slot tid % 8;
+  // X rows past M are clamped.  Four named registers per operand (not an
+  // array, which the compiler would move to LDS).
+  static_assert(kLW == 4 && kLX == 4, "the loader holds four chunks per operand");
   const int lrow = tid >> 3, slot = tid & 7;
   const uint8_t* wsrc = w + (int64_t)(n0 + lrow) * K + slot * 16;
-  int64_t xoff[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int xr = m0 + lrow + 32 * s;
-    xoff[s] = (int64_t)(xr < M ? xr : M - 1) * K + slot * 16;
-  }
-  const int64_t wstep = (int64_t)32 * K;      // 32 rows of W
-  const int st_off = chunk_addr(lrow, slot);  // rows lrow + 32 s share the swizzle (32 s & 7 == 0)
+  const int64_t wpass = (int64_t)kRP * K;
+  auto xrow = [&](int s) -> const uint8_t* {
+    const int xr = m0 + lrow + kRP * s;
+    return x + (int64_t)(xr < M ? xr : M - 1) * K + slot * 16;
+  };
+  const uint8_t* const xs0 = xrow(0);
+  const uint8_t* const xs1 = xrow(1);
+  const uint8_t* const xs2 = xrow(2);
+  const uint8_t* const xs3 = xrow(3);
+  const int st_off = chunk_addr(lrow, slot);  // rows lrow + kRP s share the swizzle
 
-  floatx16 acc[2][2];
+  floatx16 acc[kBN][kBM];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kBN; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = floatx16{};
+    for (int b = 0; b < kBM; ++b) acc[a][b] = floatx16{};
 
-  const int steps = K / kTK;
-  uint4 w0r = *(const uint4*)(wsrc), w1r = *(const uint4*)(wsrc + wstep), w2r = *(const uint4*)(wsrc + 2 * wstep),
-        w3r = *(const uint4*)(wsrc + 3 * wstep);
-  uint4 x0r = *(const uint4*)(x + xoff[0]), x1r = *(const uint4*)(x + xoff[1]), x2r = *(const uint4*)(x + xoff[2]),
-        x3r = *(const uint4*)(x + xoff[3]);
+  uint4 w0 = *(const uint4*)(wsrc), w1 = *(const uint4*)(wsrc + wpass), w2 = *(const uint4*)(wsrc + 2 * wpass),
+        w3 = *(const uint4*)(wsrc + 3 * wpass);
+  uint4 x0 = *(const uint4*)(xs0), x1 = *(const uint4*)(xs1), x2 = *(const uint4*)(xs2), x3 = *(const uint4*)(xs3);
+  constexpr int kPass = kRP * kTK;   // LDS bytes between passes
   {
-    char* dW = lds + st_off;
-    char* dX = lds + 2 * kTileB + st_off;
-    *(uint4*)(dW) = w0r, *(uint4*)(dW + 32 * kTK) = w1r, *(uint4*)(dW + 64 * kTK) = w2r, *(uint4*)(dW + 96 * kTK) = w3r;
-    *(uint4*)(dX) = x0r, *(uint4*)(dX + 32 * kTK) = x1r, *(uint4*)(dX + 64 * kTK) = x2r, *(uint4*)(dX + 96 * kTK) = x3r;
+    char* dW = ldsW + st_off;
+    char* dX = ldsX + st_off;
+    *(uint4*)(dW) = w0, *(uint4*)(dW + kPass) = w1, *(uint4*)(dW + 2 * kPass) = w2, *(uint4*)(dW + 3 * kPass) = w3;
+    *(uint4*)(dX) = x0, *(uint4*)(dX + kPass) = x1, *(uint4*)(dX + 2 * kPass) = x2, *(uint4*)(dX + 3 * kPass) = x3;
   }
   __syncthreads();
+
+  const int steps = K / kTK;
   for (int st = 0; st < steps; ++st) {
     const int buf = st & 1;
     const bool more = st + 1 < steps;
     if (more) {
       const int k0 = (st + 1) * kTK;
-      w0r = *(const uint4*)(wsrc + k0);
-      w1r = *(const uint4*)(wsrc + wstep + k0);
-      w2r = *(const uint4*)(wsrc + 2 * wstep + k0);
-      w3r = *(const uint4*)(wsrc + 3 * wstep + k0);
-      x0r = *(const uint4*)(x + xoff[0] + k0);
-      x1r = *(const uint4*)(x + xoff[1] + k0);
-      x2r = *(const uint4*)(x + xoff[2] + k0);
-      x3r = *(const uint4*)(x + xoff[3] + k0);
+      w0 = *(const uint4*)(wsrc + k0);
+      w1 = *(const uint4*)(wsrc + wpass + k0);
+      w2 = *(const uint4*)(wsrc + 2 * wpass + k0);
+      w3 = *(const uint4*)(wsrc + 3 * wpass + k0);
+      x0 = *(const uint4*)(xs0 + k0);
+      x1 = *(const uint4*)(xs1 + k0);
+      x2 = *(const uint4*)(xs2 + k0);
+      x3 = *(const uint4*)(xs3 + k0);
     }
-    const char* sW = lds + buf * kTileB;
-    const char* sX = lds + (2 + buf) * kTileB;
+    const char* sW = ldsW + buf * Cfg::kTileW;
+    const char* sX = ldsX + buf * Cfg::kTileX;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      intx8 af[2], bf[2];
+      const int ch = 4 * kk + 2 * hl;
+      intx8 bf[kBM];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int rw = wn + b * 32 + l32;
-        const int rx = wm + b * 32 + l32;
-        const int ch = 4 * kk + 2 * hl;
-        const uint4 a0 = *(const uint4*)(sW + chunk_addr(rw, ch));
-        const uint4 a1 = *(const uint4*)(sW + chunk_addr(rw, ch + 1));
-        const uint4 b0 = *(const uint4*)(sX + chunk_addr(rx, ch));
-        const uint4 b1 = *(const uint4*)(sX + chunk_addr(rx, ch + 1));
-        af[b] = intx8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      for (int b = 0; b < kBM; ++b) {
+        const int rxr = wm + b * 32 + l32;
+        const uint4 b0 = *(const uint4*)(sX + chunk_addr(rxr, ch));
+        const uint4 b1 = *(const uint4*)(sX + chunk_addr(rxr, ch + 1));
         bf[b] = intx8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
       }
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < kBN; ++a) {
+        const int rwr = wn + a * 32 + l32;
+        const uint4 a0 = *(const uint4*)(sW + chunk_addr(rwr, ch));
+        const uint4 a1 = *(const uint4*)(sW + chunk_addr(rwr, ch + 1));
+        const intx8 af = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[a], bf[b], acc[a][b], 0, 0, 0, 0, 0, 0);
+        for (int b = 0; b < kBM; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[b], acc[a][b], 0, 0, 0, 0, 0, 0);
+      }
     }
     if (more) {
-      char* dW = lds + (buf ^ 1) * kTileB + st_off;
-      char* dX = lds + (2 + (buf ^ 1)) * kTileB + st_off;
-      *(uint4*)(dW) = w0r, *(uint4*)(dW + 32 * kTK) = w1r, *(uint4*)(dW + 64 * kTK) = w2r, *(uint4*)(dW + 96 * kTK) = w3r;
-      *(uint4*)(dX) = x0r, *(uint4*)(dX + 32 * kTK) = x1r, *(uint4*)(dX + 64 * kTK) = x2r, *(uint4*)(dX + 96 * kTK) = x3r;
+      char* dW = ldsW + (buf ^ 1) * Cfg::kTileW + st_off;
+      char* dX = ldsX + (buf ^ 1) * Cfg::kTileX + st_off;
+      *(uint4*)(dW) = w0, *(uint4*)(dW + kPass) = w1, *(uint4*)(dW + 2 * kPass) = w2, *(uint4*)(dW + 3 * kPass) = w3;
+      *(uint4*)(dX) = x0, *(uint4*)(dX + kPass) = x1, *(uint4*)(dX + 2 * kPass) = x2, *(uint4*)(dX + 3 * kPass) = x3;
     }
     __syncthreads();
   }
@@ -137,12 +161,12 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_bf16_kernel(const uint8_t* 
   // m = m0 + wm + 32b + l32
   const float s = sx[0] * sw[0];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < kBM; ++b) {
     const int m = m0 + wm + b * 32 + l32;
     if (m >= M) continue;
     __bf16* yrow = y + (int64_t)m * N + n0 + wn + 4 * hl;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < kBN; ++a)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x4 v;
@@ -153,17 +177,24 @@ __global__ void __launch_bounds__(kThreads) gemm_fp8_bf16_kernel(const uint8_t* 
   }
 }
 
+template <int TN, int TM, int WTN, int WTM>
+hipError_t launch_cfg(const uint8_t* x, const uint8_t* w, const float* sx, const float* sw, void* y, int64_t M,
+                      int N, int K, hipStream_t stream) {
+  const int tiles_n = N / TN;
+  const int64_t total = (M + TM - 1) / TM * tiles_n;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_fp8_bf16_kernel<TN, TM, WTN, WTM>), dim3((unsigned)total),
+                     dim3(GemmCfg<TN, TM, WTN, WTM>::kThreads), 0, stream, x, w, sx, sw, (__bf16*)y, (int)M, N, K,
+                     tiles_n, (int)total);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_fp8_bf16(const uint8_t* x, const uint8_t* w, const float* sx, const float* sw, void* y,
                                 int64_t M, int N, int K, hipStream_t stream) {
-  const int tiles_n = N / kTN;
-  const int64_t tiles_m = (M + kTM - 1) / kTM;
-  const int64_t total = tiles_m * tiles_n;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_fp8_bf16_kernel, dim3((unsigned)total), dim3(kThreads), 0, stream, x, w, sx, sw,
-                     (__bf16*)y, (int)M, N, K, tiles_n, (int)total);
-  return hipGetLastError();
+  if (N % 256 == 0) return launch_cfg<256, 256, 128, 64>(x, w, sx, sw, y, M, N, K, stream);
+  return launch_cfg<128, 128, 64, 64>(x, w, sx, sw, y, M, N, K, stream);
 }
 
 }  // namespace skiparse

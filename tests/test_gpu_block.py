@@ -18,7 +18,7 @@ Skiparse attention) through the C ABI against oracle/block_ref.py.
   kernel's e4m3 P.  And the device block is as accurate as the oracle's:
   against the exact float64 block without quantization, its rms error is at
   most 1.2 times the oracle's.
-* The 720P-5s shape, all 24 heads: the oracle's fp8 block cannot be evaluated
+* The 720P-5s shape, all 40 heads (C = 5120): the oracle's fp8 block cannot be evaluated
   row by row (O's per-tensor scale needs every row), so sampled rows are
   checked against the exact float64 block without quantization, bars rms 0.1
   and max 0.15 (1.5 to 2 times the quantization error the oracle itself shows
@@ -233,12 +233,42 @@ def exact_block_rows(x64, ws, heads, kf, mode, tokens, theta=10000.0):
     return rows
 
 
+def test_block_480p_sampled():
+    """The 480p workload shape (21 x 32 x 52 tokens, 12 heads of 128, C = 1536,
+    k = 2 group-wise): sampled rows against the exact block, bars as at
+    720P-5s, and exact doubling with Wo's scale halved."""
+    w = wl.WORKLOADS["480p"]
+    B, T, H, W, heads, d = w.shape
+    C = heads * d
+    codes, scales, deq, _ = weights(C, 811)
+    x, x64 = bf16_input((1, T, H, W, C), 812, 0)
+    xd = x.to(DEV)
+    blockf = sk.BlockFP8(codes, scales, heads, 2, ref.GROUP)
+    y1 = blockf(xd)
+    torch.cuda.synchronize()
+    yh = y1.float().cpu().numpy().reshape(T * H * W, C)
+    assert np.all(np.isfinite(yh))
+    rng = np.random.Generator(np.random.PCG64(813))
+    members, _ = ref._members_for((T, H, W, 2, ref.GROUP))
+    tokens = np.sort(np.concatenate([rng.choice(members[s], size=12, replace=False) for s in (0, 3)]))
+    want = exact_block_rows(x64, deq, heads, 2, ref.GROUP, tokens)
+    r, m = rms_err(yh[tokens], want), max_err(yh[tokens], want)
+    print(f"480p block sampled rows vs exact: rms {r:.4f} max {m:.4f}")
+    assert r <= 0.1 and m <= 0.15
+    scales2 = scales.clone()
+    scales2[3, 1] *= 2.0
+    blockf.w_scales = scales2
+    y2 = blockf(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.float(), 2.0 * y1.float())
+
+
 @pytest.mark.skip(reason="the block's first version, with its projections on hipBLASLt, faulted the GPU at this "
                          "shape; no mistake in the block's own kernels was found by reading them (their indexing "
                          "is checked on the CPU at this shape), the projections now run on the library's own GEMM, "
                          "tested on its own at this shape, and this case stays off the GPU until a cause is shown")
 def test_block_workload_sampled():
-    """720P-5s (21 x 45 x 80 tokens, 24 heads of 128, k = 2 token-wise): rows
+    """720P-5s (21 x 45 x 80 tokens, 40 heads of 128, k = 2 token-wise): rows
     against the exact block, and exact doubling with Wo's scale halved."""
     w = wl.WORKLOADS["720p_5s"]
     B, T, H, W, heads, d = w.shape

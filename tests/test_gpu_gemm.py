@@ -83,7 +83,7 @@ def test_gemm_extreme_codes():
 
 def test_gemm_projection_shape_sampled():
     """The block's projection at 720P-5s: M = 21 * 45 * 80 tokens,
-    N = K = 24 heads * 128; sampled rows, the last tile's rows included."""
+    N = K = 40 heads * 128; sampled rows, the last tile's rows included."""
     w = wl.WORKLOADS["720p_5s"]
     B, T, H, W, heads, d = w.shape
     M, C = B * T * H * W, heads * d
