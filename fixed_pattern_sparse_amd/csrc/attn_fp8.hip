@@ -3,17 +3,25 @@
 // 方法步骤详情 method steps, with HiF8 replaced by e4m3), fp32 accumulation,
 // bf16 output, on CDNA4 (gfx950) matrix cores.
 //
-// Same decomposition and pipeline as the bf16 kernel: 8 waves x 32 queries
-// per work-group, 64-key tiles staged through registers into double-buffered
-// LDS, rows gathered by the rearrange's index function.  Per tile and 32-query
-// block:
+// Same decomposition as the bf16 kernel: 8 waves x 32 queries per
+// work-group, 64-key tiles staged through registers into LDS, rows gathered
+// by the rearrange's index function.  Per tile and 32-query block:
 //   S^T = K Q^T     2 x v_mfma_f32_32x32x64_f8f6f4 per 32 keys (d = 128);
 //                   the Q and K descales are folded into the exp2 constant;
-//   online softmax  as in the bf16 kernel (lazily raised running max, so
-//                   p <= 256 fits e4m3 without saturation);
+//   online softmax  lazily raised running max (raised when a tile's max
+//                   exceeds it by more than 2^8), so p <= 256 fits e4m3
+//                   without saturation;
 //   O^T += V^T P^T  P^T rounded to e4m3 (v_cvt_pk_fp8_f32, nearest even) in
 //                   registers; V^T from row-major V in LDS through
 //                   ds_read_b64_tr_b8; the V descale is applied with 1/l.
+// At fp8 rates the softmax's VALU work outweighs the matrix work, so the
+// loop is software-pipelined: iteration j issues the QK MFMAs of tile j in
+// the same block as the exp chain of tile j - 1, whose S came from the
+// previous iteration, then PV of tile j - 1.  Tiles rotate through a ring of
+// three LDS buffers (QK reads tile j, PV reads tile j - 1, the loader fills
+// tile j + 1), so one barrier per tile suffices.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace skiparse {
@@ -35,7 +43,7 @@ constexpr int kRowB = D;             // bytes per row
 constexpr int kTileB = kBN * kRowB;  // 8 KB per K or V tile
 constexpr int kCH = kRowB / 16;      // 16-byte chunks per row
 
-__shared__ __attribute__((aligned(16))) char gKV8[4 * kTileB];   // K0 K1 V0 V1
+__shared__ __attribute__((aligned(16))) char gKV8[6 * kTileB];   // ring of 3 x (K, V)
 __shared__ int32_t gRowBase8[kRowCap];
 __shared__ int32_t gColMap8[kColCap];
 
@@ -91,8 +99,8 @@ attn_fwd_fp8_kernel(const AttnArgs a) {
   };
   auto stash = [&](const Stage& st, int buf) {
     const int slot = lslot ^ swz(lrow);
-    *(uint4*)(gKV8 + buf * kTileB + lrow * kRowB + slot * 16) = st.k;
-    *(uint4*)(gKV8 + (2 + buf) * kTileB + lrow * kRowB + slot * 16) = st.v;
+    *(uint4*)(gKV8 + (2 * buf) * kTileB + lrow * kRowB + slot * 16) = st.k;
+    *(uint4*)(gKV8 + (2 * buf + 1) * kTileB + lrow * kRowB + slot * 16) = st.v;
   };
 
   const Stage first = fetch(0);
@@ -122,45 +130,26 @@ attn_fwd_fp8_kernel(const AttnArgs a) {
   for (int db = 0; db < 4; ++db) acc[db] = floatx16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int j = 0; j < nkv; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < nkv;
-    Stage nxt;
-    if (more) nxt = fetch(j + 1);
-    const char* sK = gKV8 + buf * kTileB;
-    const char* sV = gKV8 + (2 + buf) * kTileB;
-
-    // S^T = K Q^T
-    floatx16 s[2] = {floatx16{}, floatx16{}};
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int row = mb * 32 + l32;
-        const int c0 = (4 * kk + 2 * hl) ^ swz(row);
-        const int c1 = (4 * kk + 2 * hl + 1) ^ swz(row);
-        const uint4 lo = *(const uint4*)(sK + row * kRowB + c0 * 16);
-        const uint4 hi = *(const uint4*)(sK + row * kRowB + c1 * 16);
-        const intx8 kf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[kk], s[mb], 0, 0, 0, 0, 0, 0);
-      }
-    }
-
-    // online softmax (log2 domain)
-    if ((j + 1) * kBN > n) {
+  // One pipeline step: the online softmax of tile jsm on ssm (masked when it
+  // is the last tile), with S^T = K Q^T of the next tile issued into sqk from
+  // ring buffer kbuf in the same block as the exp chain (DoQk), then
+  // O^T += V^T P^T with V of tile jsm from ring buffer vbuf.
+  auto step = [&](auto DoQk, auto Mask, int jsm, floatx16 (&ssm)[2], int vbuf, int kbuf, floatx16 (&sqk)[2])
+      __attribute__((always_inline)) {
+    if constexpr (decltype(Mask)::value) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = j * kBN + mb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-          if (key >= n) s[mb][i] = -INFINITY;
+          const int key = jsm * kBN + mb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+          if (key >= n) ssm[mb][i] = -INFINITY;
         }
     }
-    float mx = s[0][0];
+    float mx = ssm[0][0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, ssm[0][i]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, ssm[1][i]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -177,7 +166,24 @@ attn_fwd_fp8_kernel(const AttnArgs a) {
         for (int i = 0; i < 16; ++i) acc[db][i] = __builtin_fmaf(acc[db][i], alpha, 0.0f);
     }
     const float mneg = -m_run;
-    // P^T as e4m3: byte e of lane-half h is key 32*(e/16) + 8*((e%16)/4) + 4*h + e%4
+    if constexpr (decltype(DoQk)::value) {
+      const char* sK = gKV8 + (2 * kbuf) * kTileB;
+      sqk[0] = floatx16{};
+      sqk[1] = floatx16{};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int row = mb * 32 + l32;
+          const int c0 = (4 * kk + 2 * hl) ^ swz(row);
+          const int c1 = (4 * kk + 2 * hl + 1) ^ swz(row);
+          const uint4 lo = *(const uint4*)(sK + row * kRowB + c0 * 16);
+          const uint4 hi = *(const uint4*)(sK + row * kRowB + c1 * 16);
+          const intx8 kf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sqk[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[kk], sqk[mb], 0, 0, 0, 0, 0, 0);
+        }
+      }
+    }
     intx8 pf;
     float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
@@ -186,7 +192,7 @@ attn_fwd_fp8_kernel(const AttnArgs a) {
       for (int q4 = 0; q4 < 4; ++q4) {
         float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][q4 * 4 + e], c, mneg));
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(ssm[mb][q4 * 4 + e], c, mneg));
         if (mb == 0) lsum0 += (p[0] + p[1]) + (p[2] + p[3]);
         else lsum1 += (p[0] + p[1]) + (p[2] + p[3]);
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
@@ -194,18 +200,16 @@ attn_fwd_fp8_kernel(const AttnArgs a) {
         pf[mb * 4 + q4] = w;
       }
     l_run += lsum0 + lsum1;
-
-    // O^T += V^T P^T: byte e of the A operand is V[key(e)][d], gathered by
-    // ds_read_b64_tr_b8 (4 reads of 8 keys each)
+    const char* sV = gKV8 + (2 * vbuf + 1) * kTileB;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       intx8 vf;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int jl = lane & 15;
-        const int rsel = jl >> 1;   // the row this lane addresses, 0..7
+        const int rsel = jl >> 1;
         const int row = 32 * (x >> 1) + 16 * (x & 1) + 8 * (rsel >> 2) + 4 * hl + (rsel & 3);
-        const int col = db * 32 + ((lane >> 4) & 1) * 16 + (jl & 1) * 8;   // bytes
+        const int col = db * 32 + ((lane >> 4) & 1) * 16 + (jl & 1) * 8;
         const int ch = (col >> 4) ^ swz(row);
         const intx2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (lds_intx2*)(sV + row * kRowB + ch * 16 + (col & 15)));
@@ -214,9 +218,61 @@ attn_fwd_fp8_kernel(const AttnArgs a) {
       }
       acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, acc[db], 0, 0, 0, 0, 0, 0);
     }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
 
-    if (more) stash(nxt, buf ^ 1);
+  // S^T of tile 0 on its own
+  floatx16 sa[2], sb[2];
+  {
+    const char* sK = gKV8;
+    sa[0] = floatx16{};
+    sa[1] = floatx16{};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = mb * 32 + l32;
+        const int c0 = (4 * kk + 2 * hl) ^ swz(row);
+        const int c1 = (4 * kk + 2 * hl + 1) ^ swz(row);
+        const uint4 lo = *(const uint4*)(sK + row * kRowB + c0 * 16);
+        const uint4 hi = *(const uint4*)(sK + row * kRowB + c1 * 16);
+        const intx8 kf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sa[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[kk], sa[mb], 0, 0, 0, 0, 0, 0);
+      }
+  }
+  if (nkv > 1) stash(fetch(1), 1);
+  __syncthreads();
+
+  // Iteration j (1 <= j < nkv): softmax/PV of tile j - 1 (buffer b0) with
+  // QK(j) (buffer b1) issued inside it; tile j + 1 goes to buffer b2, last
+  // read in iteration j - 1.  Unrolled by two so the S sets alternate
+  // without copies.
+  int b0 = 0, b1 = 1, b2 = 2;
+  int j = 1;
+  auto iter = [&](floatx16 (&ssm)[2], floatx16 (&sqk)[2]) __attribute__((always_inline)) {
+    const bool more = j + 1 < nkv;
+    Stage nx;
+    if (more) nx = fetch(j + 1);
+    step(T_{}, F_{}, j - 1, ssm, b0, b1, sqk);
+    if (more) stash(nx, b2);
     __syncthreads();
+    const int t = b0;
+    b0 = b1;
+    b1 = b2;
+    b2 = t;
+    ++j;
+  };
+  while (j + 1 < nkv) {
+    iter(sa, sb);
+    iter(sb, sa);
+  }
+  // the last tile: its S is in sa when nkv is odd, in sb when even
+  if (j < nkv) {
+    iter(sa, sb);
+    step(F_{}, T_{}, nkv - 1, sb, b0, b1, sa);
+  } else {
+    step(F_{}, T_{}, nkv - 1, sa, b0, b1, sb);
   }
 
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
