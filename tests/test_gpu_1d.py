@@ -12,7 +12,7 @@ import fixed_pattern_sparse_amd as sk
 import workloads as wl
 from oracle import skiparse_bwd as bwd
 from oracle import skiparse_ref as ref
-from test_gpu_bwd import LSE_TOL, check_full_size, inputs, np64, rel_err
+from test_gpu_bwd import check_full_size, check_lse, inputs, np64, rel_err
 from test_gpu_fp8 import oracle_dequant
 from test_gpu_parity import TOL, check_sampled, err_ratio, run, to_np64, workload_inputs
 
@@ -89,7 +89,7 @@ def test_bwd_small_1d(shp, kf, mode):
     grads = sk.attention_bwd(qd, kd, vd, out, dod, lse, kf, mode)
     torch.cuda.synchronize()
     want = bwd.skiparse_attention_bwd(np64(q), np64(k), np64(v), np64(do), kf, mode)
-    np.testing.assert_allclose(lse.cpu().numpy(), bwd.attention_lse(np64(q), np64(k), kf, mode), rtol=0, atol=LSE_TOL)
+    check_lse(lse.cpu().numpy(), q, k, kf, mode)
     for name, g, w_ in zip(("dq", "dk", "dv"), grads, want):
         assert rel_err(np64(g), w_) <= 2e-2, name
 

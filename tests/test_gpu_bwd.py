@@ -2,9 +2,12 @@
 pass (dQ, dK, dV) through the C ABI, against the oracle's float64 gradients
 (oracle/skiparse_bwd.py) on the same bf16 inputs.
 
-Bars.  Log-sum-exp: within 2^-9 (absolute): the kernel's denominator sums
-the bf16-rounded weights its PV product uses, each within 2^-9 relative of the
-exact one, so log l is within 2^-9 of the exact value.  Gradients: max|g - g_ref| <= 2e-2 * max|g_ref| per tensor, the
+Bars.  Log-sum-exp: within 2^-8 (absolute, natural log): the kernel's
+denominator sums the bf16-rounded weights its PV product uses, each within
+2^-8 relative of the exact one (bf16 keeps 8 significant bits, so rounding to
+nearest moves a value by at most 2^-8 of it), so log l is within 2^-8 of the
+exact value; the scores themselves are exact products of the bf16 inputs
+accumulated in fp32.  Gradients: max|g - g_ref| <= 2e-2 * max|g_ref| per tensor, the
 bf16 bar taken relative to the tensor's largest entry (gradients are often
 well below 1, where a max(1, .) normalisation would not test anything).  The
 kernels see the bf16 output O of the forward pass, the oracle the exact one;
@@ -26,7 +29,12 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 TOL = 2e-2
-LSE_TOL = 2.0 ** -9
+LSE_TOL = 2.0 ** -8
+
+
+def check_lse(got, q, k, kf, mode):
+    want = bwd.attention_lse(np64(q), np64(k), kf, mode)
+    np.testing.assert_allclose(np.asarray(got, np.float64), want, rtol=0, atol=LSE_TOL)
 
 
 def rel_err(got, want):
@@ -67,8 +75,7 @@ def test_fwd_lse_small(shp, kf, mode):
     plain = sk.attention(q.to(DEV), k.to(DEV), v.to(DEV), kf, mode)
     torch.cuda.synchronize()
     assert torch.equal(out, plain)                      # the same kernel, LSE written on the side
-    want = bwd.attention_lse(np64(q), np64(k), kf, mode)
-    np.testing.assert_allclose(lse.cpu().numpy(), want, rtol=0, atol=LSE_TOL)
+    check_lse(lse.cpu().numpy(), q, k, kf, mode)
 
 
 @pytest.mark.parametrize("shp,kf,mode", SMALL)
