@@ -19,6 +19,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libskiparse.so")
+# a plain C caller of the ABI (tests/c_caller.c), linked against the library
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_caller.c")
+C_CALLER = os.path.join(HERE, "c_caller")
 
 SOURCES = ["api.hip", "attn_bf16.hip", "block_fp8.hip", "gemm_fp8.hip", "attn_bwd.hip", "attn_f32.hip", "attn_fp8.hip", "index_map.hip", "quant_fp8.hip"]
 
@@ -63,6 +66,11 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    if os.path.exists(C_CALLER_SRC) and shutil.which("gcc"):
+        _run(["gcc", "-std=c99", "-O1", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+              "-I", "/opt/rocm/include", C_CALLER_SRC, "-o", C_CALLER + ".tmp", "-L", HERE, "-lskiparse",
+              "-L", "/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN", "-Wl,-rpath,/opt/rocm/lib"])
+        os.replace(C_CALLER + ".tmp", C_CALLER)
     if verbose:
         print("built", LIB)
     return LIB
