@@ -65,6 +65,7 @@ SMALL = [
     ((1, 1, 1, 1, 1, 128), 2, 0),        # one token: three empty subsequences
     ((1, 4, 2, 3, 2, 128), 4, 1),        # most subsequences empty
     ((1, 2, 4, 16, 1, 128), 2, 1),       # 32-member subsequences: exact tiles
+    ((1, 2, 70, 66, 1, 128), 8, 0),      # k = 8: 64 subsequences, heavy padding
 ]
 
 

@@ -37,6 +37,7 @@ SMALL = [
     ((1, 2, 10, 10, 2, 128), 1, 0),
     ((1, 5, 8, 40, 1, 128), 4, 0),
     ((1, 1, 1, 1, 1, 128), 2, 0),
+    ((1, 2, 70, 66, 1, 128), 8, 1),     # k = 8: 64 subsequences, heavy padding
 ]
 
 

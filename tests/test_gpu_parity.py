@@ -101,6 +101,8 @@ SMALL_BF16 = [
     ((1, 2, 9, 17, 2, 64), 3, 1),
     ((1, 1, 1, 1, 1, 128), 2, 0),       # one token: three empty subsequences
     ((1, 4, 2, 3, 2, 128), 4, 1),       # most subsequences empty
+    ((1, 2, 70, 66, 1, 128), 8, 0),     # k = 8: 64 subsequences, H and W padded to 128
+    ((1, 2, 70, 66, 1, 128), 8, 1),
 ]
 
 
