@@ -101,6 +101,39 @@ SubGeom make_sub(const skiparse_plan& p, int s) {
   return sg;
 }
 
+// Range and scale checks shared by the entry points that run the attention;
+// fills the call-wide part of AttnArgs (geometry, subsequences, scale) and
+// leaves every pointer NULL.
+int fill_attn_args(const skiparse_plan* plan, float softmax_scale, int32_t sub_begin, int32_t& sub_count,
+                   AttnArgs& a) {
+  if (sub_count == 0) {
+    if (sub_begin != 0) return fail(SKIPARSE_EINVAL, "sub_count == 0 (all) needs sub_begin == 0");
+    sub_count = plan->n_sub;
+  }
+  if (sub_begin < 0 || sub_count < 0 || sub_begin + sub_count > plan->n_sub)
+    return fail(SKIPARSE_EINVAL, "subsequence range [%d, %d) outside [0, %d)", sub_begin, sub_begin + sub_count, plan->n_sub);
+  if (!(std::isfinite(softmax_scale))) return fail(SKIPARSE_EINVAL, "softmax_scale must be finite");
+  const int d = plan->d;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
+  std::memset(&a, 0, sizeof a);
+  a.batch_stride = (int64_t)plan->T * plan->H * plan->W * plan->heads * d;
+  a.row_stride = plan->heads * d;
+  a.heads = plan->heads;
+  a.n_run = sub_count;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  make_geom(*plan, a.g);
+  for (int i = 0; i < sub_count; ++i) a.sub[i] = make_sub(*plan, sub_begin + i);
+  return SKIPARSE_OK;
+}
+
+// The training entry points: bf16 only, then the common part.
+int training_args(const skiparse_plan* plan, skiparse_dtype dtype, float softmax_scale, int32_t sub_begin,
+                  int32_t& sub_count, AttnArgs& a) {
+  if (dtype != SKIPARSE_BF16) return fail(SKIPARSE_EUNSUPPORTED, "training calls are built for BF16 only");
+  return fill_attn_args(plan, softmax_scale, sub_begin, sub_count, a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,30 +263,13 @@ int skiparse_attn_fwd(const skiparse_plan* plan, skiparse_dtype dtype, const voi
   if (overlap(o, numel * out_elt, q, numel * in_elt) || overlap(o, numel * out_elt, k, numel * in_elt) ||
       overlap(o, numel * out_elt, v, numel * in_elt))
     return fail(SKIPARSE_EINVAL, "o must not overlap q, k or v");
-  if (sub_count == 0) {
-    if (sub_begin != 0) return fail(SKIPARSE_EINVAL, "sub_count == 0 (all) needs sub_begin == 0");
-    sub_count = plan->n_sub;
-  }
-  if (sub_begin < 0 || sub_count < 0 || sub_begin + sub_count > plan->n_sub)
-    return fail(SKIPARSE_EINVAL, "subsequence range [%d, %d) outside [0, %d)", sub_begin, sub_begin + sub_count, plan->n_sub);
-  if (!(std::isfinite(softmax_scale))) return fail(SKIPARSE_EINVAL, "softmax_scale must be finite");
-  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
-
   AttnArgs a;
-  std::memset(&a, 0, sizeof a);
+  if (int e = fill_attn_args(plan, softmax_scale, sub_begin, sub_count, a)) return e;
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
   a.descale = dev_descale_qkv;
-  a.batch_stride = (int64_t)plan->T * plan->H * plan->W * plan->heads * d;
-  a.row_stride = plan->heads * d;
-  a.heads = plan->heads;
-  a.n_run = sub_count;
-  a.scale = scale;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  make_geom(*plan, a.g);
-  for (int i = 0; i < sub_count; ++i) a.sub[i] = make_sub(*plan, sub_begin + i);
 
   (void)hipGetLastError();   // drop an error left by unrelated earlier work
   hipError_t e;
@@ -268,32 +284,6 @@ int skiparse_attn_fwd(const skiparse_plan* plan, skiparse_dtype dtype, const voi
 }
 
 namespace {
-
-// Range, scale and common-pointer checks shared by the training entry points;
-// fills the call-wide part of AttnArgs.
-int training_args(const skiparse_plan* plan, skiparse_dtype dtype, float softmax_scale, int32_t sub_begin,
-                  int32_t& sub_count, AttnArgs& a) {
-  if (dtype != SKIPARSE_BF16) return fail(SKIPARSE_EUNSUPPORTED, "training calls are built for BF16 only");
-  if (sub_count == 0) {
-    if (sub_begin != 0) return fail(SKIPARSE_EINVAL, "sub_count == 0 (all) needs sub_begin == 0");
-    sub_count = plan->n_sub;
-  }
-  if (sub_begin < 0 || sub_count < 0 || sub_begin + sub_count > plan->n_sub)
-    return fail(SKIPARSE_EINVAL, "subsequence range [%d, %d) outside [0, %d)", sub_begin, sub_begin + sub_count, plan->n_sub);
-  if (!(std::isfinite(softmax_scale))) return fail(SKIPARSE_EINVAL, "softmax_scale must be finite");
-  const int d = plan->d;
-  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
-  std::memset(&a, 0, sizeof a);
-  a.batch_stride = (int64_t)plan->T * plan->H * plan->W * plan->heads * d;
-  a.row_stride = plan->heads * d;
-  a.heads = plan->heads;
-  a.n_run = sub_count;
-  a.scale = scale;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  make_geom(*plan, a.g);
-  for (int i = 0; i < sub_count; ++i) a.sub[i] = make_sub(*plan, sub_begin + i);
-  return SKIPARSE_OK;
-}
 
 int64_t row_count(const skiparse_plan* plan) { return (int64_t)plan->B * plan->T * plan->H * plan->W * plan->heads; }
 
@@ -513,7 +503,8 @@ int skiparse_block_fwd_fp8(const skiparse_plan* plan, const void* x, const uint8
     return fail(SKIPARSE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? workspace_bytes : 0);
   if (((uintptr_t)workspace & 255u) != 0) return fail(SKIPARSE_EINVAL, "workspace must be 256-byte aligned");
   const size_t wb = (size_t)(4 * C * C);
-  if (overlap(y, mc * 2, x, mc * 2) || overlap(y, mc * 2, w_qkvo, wb) || overlap(workspace, L.total, x, mc * 2) ||
+  if (overlap(y, mc * 2, x, mc * 2) || overlap(y, mc * 2, w_qkvo, wb) || overlap(y, mc * 2, dev_w_scales, 32) ||
+      overlap(workspace, L.total, x, mc * 2) ||
       overlap(workspace, L.total, y, mc * 2) || overlap(workspace, L.total, w_qkvo, wb) ||
       overlap(workspace, L.total, dev_w_scales, 32))
     return fail(SKIPARSE_EINVAL, "y and the workspace must not overlap each other or the inputs");
@@ -528,7 +519,7 @@ int skiparse_block_fwd_fp8(const skiparse_plan* plan, const void* x, const uint8
 
   AttnArgs a;
   int32_t all = 0;
-  if (int e = training_args(plan, SKIPARSE_BF16, 0.f, 0, all, a)) return e;
+  if (int e = fill_attn_args(plan, 0.f, 0, all, a)) return e;
   a.q = c8;
   a.k = c8 + mc;
   a.v = c8 + 2 * mc;
