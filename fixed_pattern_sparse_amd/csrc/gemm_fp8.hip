@@ -9,8 +9,8 @@
 // WTN x WTM of it as (WTN/32) x (WTM/32) blocks of
 // v_mfma_scale_f32_32x32x64_f8f6f4.  K advances 128 bytes per step through
 // double-buffered LDS filled from registers loaded one step ahead; 16-byte
-// chunks are XOR-swizzled by row so 32 lanes reading one chunk column of 32
-// rows spread over all banks.  Rows of X past M are clamped on load and masked
+// chunks are XOR-swizzled by row / 2 so 16 lanes reading one chunk column of
+// 16 rows spread over all 64 banks.  Rows of X past M are clamped on load and masked
 // on store.  Tiles are handed out XCD by XCD (work-groups are dispatched to the
 // 8 XCDs round-robin), so the tiles that share rows of X run on one XCD and
 // share its L2.
@@ -30,7 +30,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 constexpr int kTK = 128;     // bytes of K per step
 constexpr int kXcd = 8;
 
-__device__ __forceinline__ int chunk_addr(int row, int chunk) { return row * kTK + ((chunk ^ (row & 7)) << 4); }
+// LDS has 64 banks of 4 bytes: two 128-byte rows share one bank line, and a
+// 16-lane group of ds_read_b128 reads 16 rows at one chunk.  Rotating the
+// chunk with row / 2 gives those 16 rows 16 distinct (row parity, chunk)
+// slots, i.e. all 64 banks once.
+__device__ __forceinline__ int chunk_addr(int row, int chunk) {
+  return row * kTK + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
 
 template <int TN, int TM, int WTN, int WTM>
 struct GemmCfg {
@@ -44,7 +50,7 @@ struct GemmCfg {
   static constexpr int kTileW = TN * kTK, kTileX = TM * kTK;
   static constexpr int kLds = 2 * (kTileW + kTileX);
   static_assert(kLW * kThreads == TN * (kTK / 16) && kLX * kThreads == TM * (kTK / 16), "loader split");
-  static_assert(kRowsPerPass % 8 == 0, "rows of one chunk slot share the swizzle");
+  static_assert(kRowsPerPass % 16 == 0, "rows of one chunk slot share the swizzle");
 };
 
 template <int TN, int TM, int WTN, int WTM>
@@ -89,7 +95,7 @@ gemm_fp8_bf16_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ 
   const uint8_t* const xs1 = xrow(1);
   const uint8_t* const xs2 = xrow(2);
   const uint8_t* const xs3 = xrow(3);
-  const int st_off = chunk_addr(lrow, slot);  // rows lrow + kRP s share the swizzle
+  const int st_off = chunk_addr(lrow, slot);  // rows lrow + kRP s share the swizzle (kRP % 16 == 0)
 
   floatx16 acc[kBN][kBM];
 #pragma unroll
