@@ -47,10 +47,18 @@ __shared__ __attribute__((aligned(16))) char gKV8[6 * kTileB];   // ring of 3 x 
 __shared__ int32_t gRowBase8[kRowCap];
 __shared__ int32_t gColMap8[kColCap];
 
-// XOR swizzle of the 16-byte chunk index: rows r and r+1 share a 256-byte
-// bank line, so the slot rotates with r/2 and 16 consecutive rows read at one
-// chunk hit 16 distinct bank groups.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// XOR swizzle of the 16-byte chunk index.  LDS has 64 banks of 4 bytes, so
+// rows r and r+1 share a 256-byte bank line and the swizzle is a function of
+// i = (r/2) mod 8.  It is a bijection on 0..7, so 16 consecutive rows read at
+// one chunk (K, ds_read_b128) hit all 64 banks once.  Its bits are permuted
+// (i2, i0, i1) so that the rows {0-3, 8-11} + 16m that 32 lanes of a
+// ds_read_b64_tr_b8 of V read at two adjacent chunks also land on distinct
+// banks: with the plain r/2 rotation rows r and r+2 put chunks c and c^1 on
+// the same slot.
+__device__ __forceinline__ int swz(int r) {
+  const int i = (r >> 1) & 7;
+  return (i & 4) | ((i & 1) << 1) | ((i >> 1) & 1);
+}
 
 template <bool FAST>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
