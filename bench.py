@@ -278,6 +278,47 @@ def main():
                            "bwd_frac_bf16_peak": round(2.5 * pl.flops / (bms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
             del ot, lse, grads, ws
         extras["training_bf16"] = train
+        # the 8-bit training step (token-wise): Q, K, V and dO quantized per
+        # tensor on the device, the e4m3 forward keeping the log-sum-exp, then
+        # the backward on the codes; quantization of dO is timed with the
+        # backward, that of Q, K, V with the forward
+        pl = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, sk.MODE_TOKEN)
+        sc8 = torch.empty((3, 2), dtype=torch.float32, device="cuda")
+        dsc8 = torch.empty(2, dtype=torch.float32, device="cuda")
+        c8 = [torch.empty(q.shape, dtype=torch.uint8, device="cuda") for _ in range(4)]
+        qws = torch.empty(sk.skiparse_quant_fp8_workspace_bytes(q.numel()), dtype=torch.uint8, device="cuda")
+        ot = torch.empty_like(q)
+        lse = torch.empty((B, T * H * W, nh), dtype=torch.float32, device="cuda")
+        grads = [torch.empty_like(q) for _ in range(3)]
+        ws = torch.empty(sk.skiparse_attn_bwd_workspace_bytes(pl), dtype=torch.uint8, device="cuda")
+
+        def fwd8():
+            for i, t in enumerate((q, k, v)):
+                sk.skiparse_quant_fp8(t, c8[i], sc8[i], workspace=qws, stream=stream)
+            sk.skiparse_attn_fwd_lse_fp8(pl, c8[0], c8[1], c8[2], sc8, ot, lse, stream=stream)
+
+        def bwd8():
+            sk.skiparse_quant_fp8(do_, c8[3], dsc8, workspace=qws, stream=stream)
+            sk.skiparse_attn_bwd_fp8(pl, c8[0], c8[1], c8[2], sc8, ot, c8[3], dsc8, lse, *grads, workspace=ws,
+                                     stream=stream)
+
+        fwd8()
+        bwd8()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        for _ in range(3):
+            fwd8()
+        e[1].record(stream)
+        for _ in range(3):
+            bwd8()
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        fms, bms = e[0].elapsed_time(e[1]) / 3, e[1].elapsed_time(e[2]) / 3
+        extras["training_fp8_token"] = {
+            "fwd_lse_ms": round(fms, 3), "bwd_ms": round(bms, 3),
+            "bwd_tflops": round(2.5 * pl.flops / (bms * 1e-3) / 1e12, 2),
+            "note": "e4m3 tensors, quantization included; the backward's products run on bf16 MFMA"}
+        del sc8, dsc8, c8, qws, ot, lse, grads, ws
         del do_
         # Skiparse-1D on the same shape (the 1D rule on each frame's flattened
         # (h, w), stride k*k: the variant the 2D pattern is compared with)

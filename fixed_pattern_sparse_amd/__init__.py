@@ -16,6 +16,13 @@ The names mirror the C ABI in include/skiparse.h:
     skiparse_attn_bwd(plan, dtype, q, k, v, o, dout, lse, dq, dk, dv,
                       softmax_scale=0.0, workspace=None, sub_begin=0,
                       sub_count=0, stream=None)
+    skiparse_attn_fwd_lse_fp8(plan, q8, k8, v8, descale_qkv, o, lse,
+                              softmax_scale=0.0, sub_begin=0, sub_count=0,
+                              stream=None)
+    skiparse_attn_bwd_fp8(plan, q8, k8, v8, descale_qkv, o, dout8,
+                          descale_dout, lse, dq, dk, dv, softmax_scale=0.0,
+                          workspace=None, sub_begin=0, sub_count=0,
+                          stream=None)
     skiparse_quant_fp8_workspace_bytes(numel)
     skiparse_quant_fp8(x, y, scale, fp8_max=448.0, eps=1e-12,
                        workspace=None, stream=None)
@@ -74,6 +81,8 @@ EXPORTED = (
     "skiparse_attn_fwd_lse",
     "skiparse_attn_bwd_workspace_bytes",
     "skiparse_attn_bwd",
+    "skiparse_attn_fwd_lse_fp8",
+    "skiparse_attn_bwd_fp8",
     "skiparse_quant_fp8_workspace_bytes",
     "skiparse_quant_fp8",
     "skiparse_block_workspace_bytes",
@@ -151,6 +160,12 @@ def lib():
     L.skiparse_attn_bwd.restype = ctypes.c_int
     L.skiparse_attn_bwd.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                     vp, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, vp]
+    L.skiparse_attn_fwd_lse_fp8.restype = ctypes.c_int
+    L.skiparse_attn_fwd_lse_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int32,
+                                            ctypes.c_int32, vp]
+    L.skiparse_attn_bwd_fp8.restype = ctypes.c_int
+    L.skiparse_attn_bwd_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                        ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, vp]
     L.skiparse_quant_fp8_workspace_bytes.restype = ctypes.c_size_t
     L.skiparse_quant_fp8_workspace_bytes.argtypes = [ctypes.c_int64]
     L.skiparse_quant_fp8.restype = ctypes.c_int
@@ -257,6 +272,29 @@ def skiparse_attn_bwd(plan: SkiparsePlan, dtype: int, q, k, v, o, dout, lse, dq,
     _check(lib().skiparse_attn_bwd(ctypes.byref(plan), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                    _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), float(softmax_scale), _ptr(workspace),
                                    wb, sub_begin, sub_count, _stream(stream)))
+    return dq, dk, dv
+
+
+def skiparse_attn_fwd_lse_fp8(plan: SkiparsePlan, q8, k8, v8, descale_qkv, o, lse, softmax_scale: float = 0.0,
+                              sub_begin: int = 0, sub_count: int = 0, stream=None):
+    _check(lib().skiparse_attn_fwd_lse_fp8(ctypes.byref(plan), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale_qkv),
+                                           _ptr(o), _ptr(lse), float(softmax_scale), sub_begin, sub_count,
+                                           _stream(stream)))
+    return o, lse
+
+
+def skiparse_attn_bwd_fp8(plan: SkiparsePlan, q8, k8, v8, descale_qkv, o, dout8, descale_dout, lse, dq, dk, dv,
+                          softmax_scale: float = 0.0, workspace=None, sub_begin: int = 0, sub_count: int = 0,
+                          stream=None):
+    """Backward pass on e4m3 inputs; ``workspace`` as in skiparse_attn_bwd."""
+    if workspace is None:
+        import torch
+        workspace = torch.empty(skiparse_attn_bwd_workspace_bytes(plan), dtype=torch.uint8, device=o.device)
+    wb = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    _check(lib().skiparse_attn_bwd_fp8(ctypes.byref(plan), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale_qkv),
+                                       _ptr(o), _ptr(dout8), _ptr(descale_dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), float(softmax_scale), _ptr(workspace), wb, sub_begin, sub_count,
+                                       _stream(stream)))
     return dq, dk, dv
 
 
@@ -411,6 +449,43 @@ def attention_bwd(q, k, v, o, dout, lse, kf: int, mode: int, softmax_scale: floa
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     skiparse_attn_bwd(plan, _dtype_code(q), q.contiguous(), k.contiguous(), v.contiguous(), o.contiguous(),
                       dout.contiguous(), lse, dq, dk, dv, softmax_scale)
+    return dq, dk, dv
+
+
+def attention_train_fp8(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, fp8_max: float = 448.0,
+                        eps: float = 1e-12, plan: SkiparsePlan | None = None):
+    """8-bit training forward on (B, T, H, W, heads, d) device tensors:
+    quantize Q, K, V per tensor, then run the e4m3 attention keeping the
+    log-sum-exp.  Returns (out bf16, lse fp32 (B, T*H*W, heads), codes
+    (q8, k8, v8), scales fp32 (3, 2))."""
+    import torch
+    if q.dim() != 6 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one (B, T, H, W, heads, d) shape")
+    B, T, H, W, nh, d = q.shape
+    if plan is None:
+        plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
+    scales = torch.empty((3, 2), dtype=torch.float32, device=q.device)
+    codes = [quantize_fp8(t, fp8_max, eps, scale_out=scales[i])[0] for i, t in enumerate((q, k, v))]
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, T * H * W, nh), dtype=torch.float32, device=q.device)
+    skiparse_attn_fwd_lse_fp8(plan, codes[0], codes[1], codes[2], scales, out, lse, softmax_scale)
+    return out, lse, codes, scales
+
+
+def attention_bwd_fp8(codes, scales, o, dout, lse, kf: int, mode: int, softmax_scale: float = 0.0,
+                      fp8_max_grad: float = 448.0, eps: float = 1e-12, plan: SkiparsePlan | None = None):
+    """8-bit backward: quantize dout per tensor with the gradient maximum
+    fp8_max_grad, then run the backward on the e4m3 codes of Q, K, V (from
+    attention_train_fp8) and of dO.  Returns (dq, dk, dv) bf16."""
+    import torch
+    q8, k8, v8 = codes
+    B, T, H, W, nh, d = q8.shape
+    if plan is None:
+        plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
+    dscale = torch.empty(2, dtype=torch.float32, device=o.device)
+    dout8 = quantize_fp8(dout, fp8_max_grad, eps, scale_out=dscale)[0]
+    dq, dk, dv = (torch.empty(q8.shape, dtype=torch.bfloat16, device=o.device) for _ in range(3))
+    skiparse_attn_bwd_fp8(plan, q8, k8, v8, scales, o.contiguous(), dout8, dscale, lse, dq, dk, dv, softmax_scale)
     return dq, dk, dv
 
 

@@ -372,6 +372,90 @@ int skiparse_attn_bwd(const skiparse_plan* plan, skiparse_dtype dtype, const voi
   return ok();
 }
 
+int skiparse_attn_fwd_lse_fp8(const skiparse_plan* plan, const void* q8, const void* k8, const void* v8,
+                              const float* dev_descale_qkv, void* o, float* lse, float softmax_scale,
+                              int32_t sub_begin, int32_t sub_count, hipStream_t stream) {
+  if (int e = check_plan(plan)) return e;
+  const int d = plan->d;
+  if (d != 128) return fail(SKIPARSE_EUNSUPPORTED, "FP8 attention is built for d=128 only (d=%d)", d);
+  if (!q8 || !k8 || !v8 || !dev_descale_qkv || !o || !lse)
+    return fail(SKIPARSE_EINVAL, "q8, k8, v8, dev_descale_qkv, o and lse must be non-NULL");
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o))
+    return fail(SKIPARSE_EINVAL, "q8, k8, v8 and o must be 16-byte aligned");
+  if ((((uintptr_t)lse | (uintptr_t)dev_descale_qkv) & 3u) != 0)
+    return fail(SKIPARSE_EINVAL, "lse and dev_descale_qkv must be 4-byte aligned");
+  const int64_t n8 = row_count(plan) * d, nl = row_count(plan) * 4;
+  const void* ins[] = {q8, k8, v8, dev_descale_qkv};
+  const int64_t insz[] = {n8, n8, n8, 6 * 4};
+  for (int j = 0; j < 4; ++j)
+    if (overlap(o, n8 * 2, ins[j], insz[j]) || overlap(lse, nl, ins[j], insz[j]))
+      return fail(SKIPARSE_EINVAL, "o and lse must not overlap q8, k8, v8 or dev_descale_qkv");
+  if (overlap(o, n8 * 2, lse, nl)) return fail(SKIPARSE_EINVAL, "lse must not overlap o");
+  AttnArgs a;
+  if (int e = fill_attn_args(plan, softmax_scale, sub_begin, sub_count, a)) return e;
+  a.q = q8;
+  a.k = k8;
+  a.v = v8;
+  a.o = o;
+  a.lse = lse;
+  a.descale = dev_descale_qkv;
+  (void)hipGetLastError();
+  const hipError_t e = launch_attn_fp8(a, plan->B, d, stream);
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int skiparse_attn_bwd_fp8(const skiparse_plan* plan, const void* q8, const void* k8, const void* v8,
+                          const float* dev_descale_qkv, const void* o, const void* dout8,
+                          const float* dev_descale_dout, const float* lse, void* dq, void* dk, void* dv,
+                          float softmax_scale, void* workspace, size_t workspace_bytes, int32_t sub_begin,
+                          int32_t sub_count, hipStream_t stream) {
+  if (int e = check_plan(plan)) return e;
+  const int d = plan->d;
+  if (d != 128) return fail(SKIPARSE_EUNSUPPORTED, "the backward pass is built for d=128 only (d=%d)", d);
+  if (!q8 || !k8 || !v8 || !dev_descale_qkv || !o || !dout8 || !dev_descale_dout || !lse || !dq || !dk || !dv)
+    return fail(SKIPARSE_EINVAL,
+                "q8, k8, v8, dev_descale_qkv, o, dout8, dev_descale_dout, lse, dq, dk and dv must be non-NULL");
+  for (const void* x : {q8, k8, v8, o, dout8, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(x)) return fail(SKIPARSE_EINVAL, "q8, k8, v8, o, dout8, dq, dk and dv must be 16-byte aligned");
+  if ((((uintptr_t)lse | (uintptr_t)dev_descale_qkv | (uintptr_t)dev_descale_dout) & 3u) != 0)
+    return fail(SKIPARSE_EINVAL, "lse, dev_descale_qkv and dev_descale_dout must be 4-byte aligned");
+  const size_t need = skiparse_attn_bwd_workspace_bytes(plan);
+  if (!workspace || workspace_bytes < need)
+    return fail(SKIPARSE_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace & 3u) != 0) return fail(SKIPARSE_EINVAL, "workspace must be 4-byte aligned");
+  const int64_t n8 = row_count(plan) * d, nl = row_count(plan) * 4;
+  const void* ins[] = {q8, k8, v8, dev_descale_qkv, o, dout8, dev_descale_dout, lse};
+  const int64_t insz[] = {n8, n8, n8, 6 * 4, n8 * 2, n8, 2 * 4, nl};
+  void* outs[] = {dq, dk, dv, workspace};
+  const int64_t outsz[] = {n8 * 2, n8 * 2, n8 * 2, (int64_t)need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j]))
+        return fail(SKIPARSE_EINVAL, "outputs and workspace must not overlap the inputs, the scales or lse");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return fail(SKIPARSE_EINVAL, "dq, dk, dv and workspace must not overlap");
+  }
+  AttnArgs a;
+  if (int e = fill_attn_args(plan, softmax_scale, sub_begin, sub_count, a)) return e;
+  a.q = q8;
+  a.k = k8;
+  a.v = v8;
+  a.descale = dev_descale_qkv;
+  a.o = const_cast<void*>(o);   // read only by the backward kernels
+  a.dout = dout8;
+  a.descale_do = dev_descale_dout;
+  a.lse = const_cast<float*>(lse);
+  a.dsum = (float*)workspace;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  (void)hipGetLastError();
+  const hipError_t e = launch_attn_bwd_fp8(a, plan->B, d, stream);
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t skiparse_quant_fp8_workspace_bytes(int64_t numel) { return quant_workspace_bytes(numel < 0 ? 0 : numel); }
 
 int skiparse_quant_fp8(const void* x, skiparse_dtype x_dtype, int64_t numel, uint8_t* y, float* dev_scale,

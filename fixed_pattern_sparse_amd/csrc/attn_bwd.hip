@@ -23,11 +23,21 @@
 //                        and dO (with L and D); S = Q K^T + (-L/c),
 //                        P = exp2(c S), dV^T += dO^T P, dP = dO V^T + (-D),
 //                        dK^T += Q^T (P * dP).
+// 8-bit inputs (F8): Q, K, V and dO arrive as per-tensor e4m3 codes with
+// their scales (the pages quantize every tensor of the 8-bit training path
+// per tensor, the gradient with its own maximum).  The loaders widen each code
+// to bf16, which is exact (every e4m3 value is a bf16 value), so the MFMA
+// products of codes are exact as on the 8-bit matrix core; the descales fold
+// into scalars: the exp2 constant takes 1/(s_q s_k), D enters as D / f with
+// f = 1/(s_do s_v) so dP - D is f (dO^ V^T - D/f), and the outputs take
+// scale f / s_k (dQ), scale f / s_q (dK) and 1/s_do (dV).
 // Per-query L and D enter the dK/dV kernel through the MFMA accumulator's
 // initial value, so they cost no registers of their own.  Each staged tile is
 // read both row-major (ds_read_b128, 16 rows at one chunk) and transposed
 // (ds_read_b64_tr_b16, 4 rows x 4 chunks), and one XOR swizzle of the 16-byte
 // chunk index serves both without bank conflicts.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace skiparse {
@@ -64,6 +74,48 @@ __shared__ int32_t gTokB[kTokCap];
 // 16 consecutive rows map to 16 distinct chunks (row-major reads), and each
 // aligned group of 4 rows differs in bits 3:2 (transposed reads of 4 chunks).
 __device__ __forceinline__ int uswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Two e4m3 codes (bytes 2*hi, 2*hi + 1 of w) as two bf16 values.  An e4m3
+// value has at most 4 significant bits and an exponent within bf16's range,
+// so its fp32 form ends in 16 zero bits and the high halves are exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16x2(uint32_t w) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+// Eight consecutive elements starting at element offset e of a row-major
+// tensor as loaded (8 bytes of e4m3 codes or 16 of bf16), and widened to
+// eight bf16 values.  The streamed tiles keep the loaded form in registers
+// and widen it only when they store it to LDS, after the tile's compute, so
+// the load's latency stays hidden as it is for bf16.
+template <bool F8>
+using Raw8 = typename std::conditional<F8, uint2, uint4>::type;
+
+template <bool F8>
+__device__ __forceinline__ Raw8<F8> load_raw8(const char* base, int64_t e) {
+  if constexpr (F8) return *(const uint2*)(base + e);
+  else return *(const uint4*)(base + e * 2);
+}
+
+template <bool F8>
+__device__ __forceinline__ uint4 widen8(Raw8<F8> c) {
+  if constexpr (F8)
+    return uint4{e4m3x2_bf16x2<false>(c.x), e4m3x2_bf16x2<true>(c.x), e4m3x2_bf16x2<false>(c.y),
+                 e4m3x2_bf16x2<true>(c.y)};
+  else return c;
+}
+
+template <bool F8>
+__device__ __forceinline__ uint4 load8(const char* base, int64_t e) {
+  return widen8<F8>(load_raw8<F8>(base, e));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
+  bf16x8 f;
+  __builtin_memcpy(&f, &u, 16);
+  return f;
+}
 
 // A fragment of a staged tile read row-major: rows l32 (+0), chunk 2*kk + hl.
 __device__ __forceinline__ bf16x8 frag_rows(const char* t, int l32, int hl, int kk) {
@@ -112,8 +164,11 @@ __device__ __forceinline__ void store_rows_t(__bf16* dst, const floatx16 (&acc)[
 // D = rowsum(dO * O) for every (b, token, head) row
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256) bwd_dsum_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                       float* __restrict__ dsum, int64_t rows) {
+// (F8: dO as e4m3 codes, and D / f = s_v * rowsum(dO^ * O) is written.)
+template <bool F8>
+__global__ void __launch_bounds__(256) bwd_dsum_kernel(const __bf16* __restrict__ o, const void* __restrict__ dout,
+                                                       const float* __restrict__ descale, float* __restrict__ dsum,
+                                                       int64_t rows) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
@@ -123,13 +178,13 @@ __global__ void __launch_bounds__(256) bwd_dsum_kernel(const __bf16* __restrict_
     float acc = 0.f;
     if (r < rows) {
       const bf16x8 x = *(const bf16x8*)(o + r * D + ch * 8);
-      const bf16x8 y = *(const bf16x8*)(dout + r * D + ch * 8);
+      const bf16x8 y = as_bf16x8(load8<F8>((const char*)dout, r * D + ch * 8));
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
     }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (r < rows && ch == 0) dsum[r] = acc;
+    if (r < rows && ch == 0) dsum[r] = F8 ? acc * descale[4] : acc;
   }
 }
 
@@ -161,7 +216,7 @@ struct Rows {
 // dQ: queries fixed, key tiles streamed
 // ---------------------------------------------------------------------------
 
-template <int ROWS>
+template <int ROWS, bool F8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(const AttnArgs a) {
   const int tid = threadIdx.x;
@@ -177,21 +232,22 @@ attn_bwd_dq_kernel(const AttnArgs a) {
   const int64_t N = (int64_t)a.g.T * a.g.H * a.g.W;
   const int64_t base = (int64_t)wi.b * a.batch_stride + (int64_t)wi.head * D;
   const int64_t rs = a.row_stride;
-  const __bf16* __restrict__ qp = (const __bf16*)a.q + base;
-  const __bf16* __restrict__ dop = (const __bf16*)a.dout + base;
-  const char* __restrict__ kb = (const char*)((const __bf16*)a.k + base);
-  const char* __restrict__ vb = (const char*)((const __bf16*)a.v + base);
+  constexpr int EB = F8 ? 1 : 2;   // bytes per element
+  const char* __restrict__ qb = (const char*)a.q + base * EB;
+  const char* __restrict__ dob = (const char*)a.dout + base * EB;
+  const char* __restrict__ kb = (const char*)a.k + base * EB;
+  const char* __restrict__ vb = (const char*)a.v + base * EB;
 
   Rows<ROWS> rows(a, sg, n);
   rows.build(tid);
   const int lrow = tid / kCH, lslot = tid % kCH;
   const int sw_st = (lslot ^ uswz(lrow)) * 16;
-  auto fetch = [&](int tile, uint4& kx, uint4& vx) {
-    const int64_t off = (int64_t)rows.tok(tile * kBT + lrow) * rs * 2 + lslot * 16;
-    kx = *(const uint4*)(kb + off);
-    vx = *(const uint4*)(vb + off);
+  auto fetch = [&](int tile, Raw8<F8>& kx, Raw8<F8>& vx) {
+    const int64_t e = (int64_t)rows.tok(tile * kBT + lrow) * rs + lslot * 8;
+    kx = load_raw8<F8>(kb, e);
+    vx = load_raw8<F8>(vb, e);
   };
-  uint4 kx, vx;
+  Raw8<F8> kx, vx;
   fetch(0, kx, vx);
 
   // the lane's query: Q and dO fragments (B operands), L and D
@@ -202,17 +258,17 @@ attn_bwd_dq_kernel(const AttnArgs a) {
   bf16x8 qf[KK], dof[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    qf[kk] = *(const bf16x8*)(qp + qoff + kk * 16 + hl * 8);
-    dof[kk] = *(const bf16x8*)(dop + qoff + kk * 16 + hl * 8);
+    qf[kk] = as_bf16x8(load8<F8>(qb, qoff + kk * 16 + hl * 8));
+    dof[kk] = as_bf16x8(load8<F8>(dob, qoff + kk * 16 + hl * 8));
     __asm__ volatile("" : "+v"(qf[kk]), "+v"(dof[kk]));
   }
   const int64_t ridx = ((int64_t)wi.b * N + tq) * a.heads + wi.head;
   const float lse2 = a.lse[ridx] * kLog2e;
   const float dq_d = a.dsum[ridx];
-  const float c = a.scale_log2;
+  const float c = F8 ? a.scale_log2 * a.descale[1] * a.descale[3] : a.scale_log2;
 
-  *(uint4*)(gA + lrow * kRowB + sw_st) = kx;
-  *(uint4*)(gB + lrow * kRowB + sw_st) = vx;
+  *(uint4*)(gA + lrow * kRowB + sw_st) = widen8<F8>(kx);
+  *(uint4*)(gB + lrow * kRowB + sw_st) = widen8<F8>(vx);
   __syncthreads();
 
   floatx16 acc[DB];
@@ -248,12 +304,13 @@ attn_bwd_dq_kernel(const AttnArgs a) {
       for (int cc = 0; cc < 2; ++cc)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols(sK, lane, hl, db, cc), dsb[cc], acc[db], 0, 0, 0);
     if (more) {
-      *(uint4*)(gA + (buf ^ 1) * kTileB + lrow * kRowB + sw_st) = kx;
-      *(uint4*)(gB + (buf ^ 1) * kTileB + lrow * kRowB + sw_st) = vx;
+      *(uint4*)(gA + (buf ^ 1) * kTileB + lrow * kRowB + sw_st) = widen8<F8>(kx);
+      *(uint4*)(gB + (buf ^ 1) * kTileB + lrow * kRowB + sw_st) = widen8<F8>(vx);
     }
     __syncthreads();
   }
-  if (qok) store_rows_t((__bf16*)a.dq + base + qoff, acc, a.scale, hl);
+  const float mul = F8 ? a.scale * a.descale_do[1] * a.descale[5] * a.descale[3] : a.scale;
+  if (qok) store_rows_t((__bf16*)a.dq + base + qoff, acc, mul, hl);
 }
 
 // ---------------------------------------------------------------------------
@@ -264,6 +321,7 @@ attn_bwd_dq_kernel(const AttnArgs a) {
 // the token table).
 // ---------------------------------------------------------------------------
 
+template <bool F8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkv_fused_kernel(const AttnArgs a) {
   const int tid = threadIdx.x;
@@ -279,36 +337,38 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
   const int64_t N = (int64_t)a.g.T * a.g.H * a.g.W;
   const int64_t base = (int64_t)wi.b * a.batch_stride + (int64_t)wi.head * D;
   const int64_t rs = a.row_stride;
-  const char* __restrict__ qb = (const char*)((const __bf16*)a.q + base);
-  const char* __restrict__ db_ = (const char*)((const __bf16*)a.dout + base);
-  const char* __restrict__ vb = (const char*)((const __bf16*)a.v + base);
-  const float c = a.scale_log2;
+  constexpr int EB = F8 ? 1 : 2;   // bytes per element
+  const char* __restrict__ qb = (const char*)a.q + base * EB;
+  const char* __restrict__ db_ = (const char*)a.dout + base * EB;
+  const char* __restrict__ vb = (const char*)a.v + base * EB;
+  const char* __restrict__ kb = (const char*)a.k + base * EB;
+  const float c = F8 ? a.scale_log2 * a.descale[1] * a.descale[3] : a.scale_log2;
   const float inv_c = 1.0f / c;
   Rows<0> rows(a, sg, n);
 
   const int lrow = tid / kCH, lslot = tid % kCH;
   const int sw_st = (lslot ^ uswz(lrow)) * 16;
-  auto fetch = [&](int tile, uint4& qx, uint4& dx, float& ln, float& dn) {
+  auto fetch = [&](int tile, Raw8<F8>& qx, Raw8<F8>& dx, float& ln, float& dn) {
     const int j = tile * kBT + lrow;
     const int t = rows.tok(j);
-    const int64_t off = (int64_t)t * rs * 2 + lslot * 16;
-    qx = *(const uint4*)(qb + off);
-    dx = *(const uint4*)(db_ + off);
+    const int64_t e = (int64_t)t * rs + lslot * 8;
+    qx = load_raw8<F8>(qb, e);
+    dx = load_raw8<F8>(db_, e);
     if (lslot == 0) {
       const int64_t ridx = ((int64_t)wi.b * N + t) * a.heads + wi.head;
       ln = j < n ? -(a.lse[ridx] * kLog2e) * inv_c : -INFINITY;
       dn = j < n ? -a.dsum[ridx] : 0.f;
     }
   };
-  auto stash = [&](int buf, const uint4& qx, const uint4& dx, float ln, float dn) {
-    *(uint4*)(gA + buf * kTileB + lrow * kRowB + sw_st) = qx;
-    *(uint4*)(gB + buf * kTileB + lrow * kRowB + sw_st) = dx;
+  auto stash = [&](int buf, const Raw8<F8>& qx, const Raw8<F8>& dx, float ln, float dn) {
+    *(uint4*)(gA + buf * kTileB + lrow * kRowB + sw_st) = widen8<F8>(qx);
+    *(uint4*)(gB + buf * kTileB + lrow * kRowB + sw_st) = widen8<F8>(dx);
     if (lslot == 0) {
       gL[buf * kBT + lrow] = ln;
       gDn[buf * kBT + lrow] = dn;
     }
   };
-  uint4 qx, dx;
+  Raw8<F8> qx, dx;
   float ln = 0.f, dn = 0.f;
   fetch(0, qx, dx, ln, dn);
 
@@ -318,8 +378,8 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < kBM * kCH / kThreads; ++i) {
     const int r = lrow + i * kBT;
-    const int64_t off = (int64_t)rows.tok(key0 + r) * rs * 2 + lslot * 16;
-    *(uint4*)(gVk + r * kRowB + (lslot ^ uswz(r)) * 16) = *(const uint4*)(vb + off);
+    const int64_t e = (int64_t)rows.tok(key0 + r) * rs + lslot * 8;
+    *(uint4*)(gVk + r * kRowB + (lslot ^ uswz(r)) * 16) = load8<F8>(vb, e);
   }
 
   const int jk = key0 + wave * 32 + l32;
@@ -328,7 +388,7 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
   bf16x8 kf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    kf[kk] = *(const bf16x8*)((const __bf16*)a.k + base + koff + kk * 16 + hl * 8);
+    kf[kk] = as_bf16x8(load8<F8>(kb, koff + kk * 16 + hl * 8));
     __asm__ volatile("" : "+v"(kf[kk]));
   }
   const char* sVk = gVk + wave * 32 * kRowB;   // the wave's 32 key rows
@@ -399,14 +459,15 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
     __syncthreads();
   }
   if (kok) {
-    store_rows_t((__bf16*)a.dk + base + koff, accK, a.scale, hl);
-    store_rows_t((__bf16*)a.dv + base + koff, accV, 1.0f, hl);
+    const float mk = F8 ? a.scale * a.descale_do[1] * a.descale[5] * a.descale[1] : a.scale;
+    const float mv = F8 ? a.descale_do[1] : 1.0f;
+    store_rows_t((__bf16*)a.dk + base + koff, accK, mk, hl);
+    store_rows_t((__bf16*)a.dv + base + koff, accV, mv, hl);
   }
 }
 
-}  // namespace
-
-hipError_t launch_attn_bwd(AttnArgs a, int B, int d, hipStream_t stream) {
+template <bool F8>
+hipError_t launch_bwd(AttnArgs a, int B, int d, hipStream_t stream) {
   if (d != D) return hipErrorNotSupported;
   // D for every row of the tensors (rows outside the run subsequences are
   // computed too and never read)
@@ -414,19 +475,25 @@ hipError_t launch_attn_bwd(AttnArgs a, int B, int d, hipStream_t stream) {
   if (rows > 0) {
     int64_t blocks = (rows + 15) / 16;
     blocks = blocks < 8192 ? blocks : 8192;
-    hipLaunchKernelGGL(bwd_dsum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const __bf16*)a.o,
-                       (const __bf16*)a.dout, a.dsum, rows);
+    hipLaunchKernelGGL(bwd_dsum_kernel<F8>, dim3((unsigned)blocks), dim3(256), 0, stream, (const __bf16*)a.o,
+                       a.dout, a.descale, a.dsum, rows);
   }
   assign_tiles(a, B, kBM);
   if (a.total_tiles == 0) return hipGetLastError();
-  const bool table = token_table_ok(a, (int64_t)a.row_stride * 2, kTokCap);
+  const bool table = token_table_ok(a, (int64_t)a.row_stride * (F8 ? 1 : 2), kTokCap);
   const dim3 grid(a.total_tiles), block(kThreads);
   if (table)
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<2, F8>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<0>), grid, block, 0, stream, a);
-  hipLaunchKernelGGL(attn_bwd_dkv_fused_kernel, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<0, F8>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_dkv_fused_kernel<F8>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_attn_bwd(AttnArgs a, int B, int d, hipStream_t stream) { return launch_bwd<false>(a, B, d, stream); }
+
+hipError_t launch_attn_bwd_fp8(AttnArgs a, int B, int d, hipStream_t stream) { return launch_bwd<true>(a, B, d, stream); }
 
 }  // namespace skiparse

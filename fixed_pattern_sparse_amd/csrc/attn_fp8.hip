@@ -119,7 +119,8 @@ attn_fwd_fp8_kernel(const AttnArgs a) {
   intx8 qf[2];
   const int jq = wi.qtile * kBM + wave * 32 + l32;
   const bool qok = jq < n;
-  const int64_t qoff = (int64_t)token_of((uint32_t)(qok ? jq : n - 1), sg, a.g) * rs;
+  const int tokq = (int)token_of((uint32_t)(qok ? jq : n - 1), sg, a.g);
+  const int64_t qoff = (int64_t)tokq * rs;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const uint4 lo = *(const uint4*)(qp + qoff + kk * 64 + hl * 32);
@@ -284,7 +285,15 @@ attn_fwd_fp8_kernel(const AttnArgs a) {
   }
 
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-  const float inv = dv / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+  const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  const float inv = dv / l_tot;
+  if (a.lse != nullptr && qok && hl == 0) {
+    // log-sum-exp of the dequantized scores in natural units: m is in log2
+    // units of s * c (c holding the softmax scale and both descales), and l
+    // sums the unrounded p, so this is the exact denominator up to fp32
+    const int64_t N = (int64_t)a.g.T * a.g.H * a.g.W;
+    a.lse[((int64_t)wi.b * N + tokq) * a.heads + wi.head] = 0.69314718055994531f * (m_run + __log2f(l_tot));
+  }
   if (qok) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)

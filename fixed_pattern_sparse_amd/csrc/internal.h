@@ -17,7 +17,8 @@ struct AttnArgs {
   const void* v;
   void* o;
   const float* descale;     // FP8 only: {s_q, 1/s_q, s_k, 1/s_k, s_v, 1/s_v} on the device
-  float* lse;               // forward (bf16): natural-log softmax denominators, (B, T*H*W, heads), or NULL
+  const float* descale_do;  // FP8 backward only: {s_do, 1/s_do} of dO on the device
+  float* lse;               // forward: natural-log softmax log-sum-exp, (B, T*H*W, heads), or NULL
   const void* dout;         // backward: upstream gradient dO, same layout as o
   float* dsum;              // backward: rowsum(dO * O), (B, T*H*W, heads), written by the first kernel
   void* dq;                 // backward outputs, same layout as q
@@ -52,6 +53,7 @@ hipError_t launch_attn_bf16(AttnArgs a, int B, int d, hipStream_t stream);
 hipError_t launch_attn_f32(AttnArgs a, int B, int d, hipStream_t stream);
 hipError_t launch_attn_fp8(AttnArgs a, int B, int d, hipStream_t stream);
 hipError_t launch_attn_bwd(AttnArgs a, int B, int d, hipStream_t stream);
+hipError_t launch_attn_bwd_fp8(AttnArgs a, int B, int d, hipStream_t stream);
 hipError_t launch_index_map(const Geom& g, const SubGeom* subs, int n_sub, int sub_h, int sub_w,
                             int32_t* out, hipStream_t stream);
 size_t quant_workspace_bytes(int64_t numel);

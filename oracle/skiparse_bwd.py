@@ -31,10 +31,13 @@ import numpy as np
 from .skiparse_ref import TOKEN, _members_for, default_scale, from_subsequences, subsequence_real_mask, to_subsequences
 
 
-def softmax_attention_bwd(q, k, v, do, scale, key_ok=None):
+def softmax_attention_bwd(q, k, v, do, scale, key_ok=None, o=None):
     """Gradients (dq, dk, dv) of O = softmax(scale * q k^T) v for upstream dO,
     in float64, the keys where ``key_ok`` is False excluded (they get zero
-    gradient).  q, do: (Lq, d); k, v: (Lk, d)."""
+    gradient).  q, do: (Lq, d); k, v: (Lk, d).  With ``o`` given (Lq, d), the
+    row term of dS is formed from it as rowsum(dO * o), the form a backward
+    pass that receives the forward's output uses (equal to rowsum(P * dP)
+    when o is the exact output); otherwise from the softmax Jacobian."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -47,21 +50,24 @@ def softmax_attention_bwd(q, k, v, do, scale, key_ok=None):
     p = p / p.sum(axis=1, keepdims=True)
     dv = p.T @ do
     dp = do @ v.T
-    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    rowterm = (p * dp).sum(axis=1, keepdims=True) if o is None else (do * np.asarray(o, np.float64)).sum(axis=1, keepdims=True)
+    ds = p * (dp - rowterm)
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     return dq, dk, dv
 
 
-def skiparse_attention_bwd(q, k, v, do, kf: int, mode: int, scale=None):
+def skiparse_attention_bwd(q, k, v, do, kf: int, mode: int, scale=None, o=None):
     """(dq, dk, dv) of Skiparse-2D attention, all (B, T, H, W, heads, d), by the
     same steps as the forward oracle: pad -> rearrange -> per-subsequence
-    gradients -> rearrange back -> crop."""
+    gradients -> rearrange back -> crop.  ``o``: optional forward output of the
+    same layout, as in :func:`softmax_attention_bwd`."""
     q = np.asarray(q, np.float64)
     B, T, H, W, nh, d = q.shape
     mode = TOKEN if kf == 1 else mode
     scale = default_scale(d) if scale is None else scale
     qs, ks, vs, dos = (to_subsequences(np.asarray(x, np.float64), kf, mode) for x in (q, k, v, do))
+    os_ = None if o is None else to_subsequences(np.asarray(o, np.float64), kf, mode)
     ok = subsequence_real_mask(T, H, W, kf, mode)
     grads = [np.zeros_like(qs) for _ in range(3)]
     for b in range(B):
@@ -72,7 +78,8 @@ def skiparse_attention_bwd(q, k, v, do, kf: int, mode: int, scale=None):
             for h in range(nh):
                 # only real queries exist; their gradients reach real keys only
                 dq, dk, dv = softmax_attention_bwd(qs[b, s, h][real], ks[b, s, h][real], vs[b, s, h][real],
-                                                   dos[b, s, h][real], scale)
+                                                   dos[b, s, h][real], scale,
+                                                   o=None if os_ is None else os_[b, s, h][real])
                 grads[0][b, s, h][real] = dq
                 grads[1][b, s, h][real] = dk
                 grads[2][b, s, h][real] = dv
@@ -99,6 +106,50 @@ def attention_lse(q, k, kf: int, mode: int, scale=None):
                 m = s.max(axis=1)
                 out[b, mem, h] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
     return out
+
+
+# ---------------------------------------------------------------------------
+# 8-bit training
+# ---------------------------------------------------------------------------
+
+def quantized_inputs(q, k, v, do=None, fp8_max=448.0, fp8_max_grad=448.0, eps=1e-12):
+    """The per-tensor 8-bit tensors of the training path (OSP-Next summary,
+    方法步骤详情 method steps: every tensor quantized as a whole with
+    scale = FP8max / (Amax + eps), the backward pass with its own maximum), by
+    the oracle's own codec (oracle.fp8_ref).  Returns a dict with the codes,
+    the fp32 scales and the dequantized float64 tensors code / scale, for Q, K,
+    V (maximum fp8_max) and, if given, dO (maximum fp8_max_grad)."""
+    from . import fp8_ref as f8
+    out = {}
+    named = [("q", q, fp8_max), ("k", k, fp8_max), ("v", v, fp8_max)]
+    if do is not None:
+        named.append(("do", do, fp8_max_grad))
+    for name, x, mx in named:
+        codes, scale, _ = f8.quantize_per_tensor(np.asarray(x, np.float32).ravel(), mx, eps)
+        out[name + "8"] = codes.reshape(np.shape(x))
+        out["s_" + name] = scale
+        out[name] = f8.dequantize(codes, scale).reshape(np.shape(x))
+    return out
+
+
+def dequantized_part(part, amax, fp8_max=448.0, eps=1e-12):
+    """Dequantized float64 values of a part of a tensor that is quantized as a
+    whole: the scale comes from the whole tensor's amax (fp32), the codes from
+    the part's own elements (per-element, so any part can be formed alone)."""
+    from . import fp8_ref as f8
+    scale = f8.per_tensor_scale(np.float32(amax), fp8_max, eps)
+    codes = f8.e4m3_encode((np.asarray(part, np.float32) * scale).astype(np.float32))
+    return f8.dequantize(codes, scale)
+
+
+def skiparse_attention_bwd_fp8(q, k, v, do, kf: int, mode: int, scale=None, fp8_max=448.0, fp8_max_grad=448.0,
+                               eps=1e-12, o=None):
+    """Gradients of the 8-bit training path: Q, K, V and dO are quantized per
+    tensor (:func:`quantized_inputs`) and the layer's gradients are those of
+    the dequantized tensors, :func:`skiparse_attention_bwd` applied to them
+    (``o`` passed through).  Returns (dq, dk, dv, the quantized-input dict)."""
+    t = quantized_inputs(q, k, v, do, fp8_max, fp8_max_grad, eps)
+    return (*skiparse_attention_bwd(t["q"], t["k"], t["v"], t["do"], kf, mode, scale, o=o), t)
 
 
 # ---------------------------------------------------------------------------

@@ -194,6 +194,63 @@ def test_attn_bwd_argument_errors():
     assert sk.skiparse_attn_bwd_workspace_bytes(bad) == 0
 
 
+def test_attn_fwd_lse_fp8_argument_errors():
+    """Validation failures of the 8-bit training forward (nothing is launched)."""
+    import ctypes
+    L = sk.lib()
+    p = sk.skiparse_plan_init(1, 2, 8, 8, 2, 128, 2, 0)
+    G = 1 << 32
+    args = dict(q=1 * G, k=2 * G, v=3 * G, ds=4 * G, o=5 * G, lse=6 * G, sb=0, sc=0, scale=0.0)
+
+    def code(plan=p, **kw):
+        a = dict(args, **kw)
+        return L.skiparse_attn_fwd_lse_fp8(ctypes.byref(plan), a["q"], a["k"], a["v"], a["ds"], a["o"], a["lse"],
+                                           a["scale"], a["sb"], a["sc"], None)
+
+    assert code(ds=0) == sk.EINVAL
+    assert code(lse=0) == sk.EINVAL
+    assert code(q=1 * G + 8) == sk.EINVAL                            # misaligned
+    assert code(ds=4 * G + 2) == sk.EINVAL
+    assert code(o=1 * G + 256) == sk.EINVAL                          # o overlaps q8
+    assert code(lse=4 * G + 8) == sk.EINVAL                          # lse overlaps the scales
+    assert code(lse=5 * G + 1024) == sk.EINVAL                       # lse overlaps o
+    assert code(sb=3, sc=2) == sk.EINVAL
+    assert code(scale=float("inf")) == sk.EINVAL
+    p64 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 64, 2, 0)
+    assert code(plan=p64) == sk.EUNSUPPORTED
+
+
+def test_attn_bwd_fp8_argument_errors():
+    """Validation failures of the 8-bit backward pass (nothing is launched)."""
+    import ctypes
+    L = sk.lib()
+    p = sk.skiparse_plan_init(1, 2, 8, 8, 2, 128, 2, 0)
+    need = sk.skiparse_attn_bwd_workspace_bytes(p)
+    G = 1 << 32
+    args = dict(q=1 * G, k=2 * G, v=3 * G, ds=4 * G, o=5 * G, do=6 * G, dds=7 * G, lse=8 * G, dq=9 * G, dk=10 * G,
+                dv=11 * G, ws=12 * G, wb=need, sb=0, sc=0)
+
+    def code(plan=p, **kw):
+        a = dict(args, **kw)
+        return L.skiparse_attn_bwd_fp8(ctypes.byref(plan), a["q"], a["k"], a["v"], a["ds"], a["o"], a["do"],
+                                       a["dds"], a["lse"], a["dq"], a["dk"], a["dv"], 0.0, a["ws"], a["wb"], a["sb"],
+                                       a["sc"], None)
+
+    assert code(dds=0) == sk.EINVAL
+    assert code(ds=0) == sk.EINVAL
+    assert code(do=6 * G + 8) == sk.EINVAL                           # misaligned
+    assert code(dds=7 * G + 1) == sk.EINVAL
+    assert code(ws=0) == sk.EWORKSPACE
+    assert code(wb=need - 4) == sk.EWORKSPACE
+    assert code(dq=1 * G + 256) == sk.EINVAL                         # dq overlaps q8
+    assert code(dk=7 * G) == sk.EINVAL                               # dk overlaps dO's scales
+    assert code(ws=4 * G) == sk.EINVAL                               # workspace overlaps the Q/K/V scales
+    assert code(dv=9 * G + 4096) == sk.EINVAL                        # dv overlaps dq
+    assert code(sb=2, sc=3) == sk.EINVAL
+    p64 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 64, 2, 0)
+    assert code(plan=p64, wb=sk.skiparse_attn_bwd_workspace_bytes(p64)) == sk.EUNSUPPORTED
+
+
 def test_quant_argument_errors():
     L = sk.lib()
     n = 1000

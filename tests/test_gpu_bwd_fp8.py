@@ -1,0 +1,229 @@
+"""GPU parity of the 8-bit training path through the C ABI: the e4m3 forward
+that keeps the log-sum-exp (skiparse_attn_fwd_lse_fp8) and the backward pass
+on e4m3 codes (skiparse_attn_bwd_fp8), against the oracle's float64 results on
+its own per-tensor quantization of the same bf16 inputs
+(oracle.skiparse_bwd.quantized_inputs: the gradients of the dequantized
+tensors).
+
+Bars.
+* Forward output: the same kernel as skiparse_attn_fwd on e4m3, bit for bit.
+* Log-sum-exp, per query i: within 2^-11 * M_i + 2^-12, where
+  M_i = max_j scale * sum_d |q_id k_jd| over the keys j of i's subsequence
+  (dequantized values).  The e4m3 MFMA sums each group of 8 products with
+  every product truncated to 14 bits below the group's largest (measured on
+  gfx950), so a score is within 2^-11 * scale * sum_d |q_d k_d| of its exact
+  value (the fp32 accumulation of the group sums adds far less), and a
+  log-sum-exp moves by at most its scores' largest error; the denominator
+  sums the unrounded exponentials in fp32 (about n * 2^-24 relative for n
+  keys, under 1e-4 here), covered by the 2^-12.
+* Backward alone: the kernels get the oracle's O (rounded to bf16) and LSE,
+  and the oracle forms the row term of dS from that same O (rowsum(dO * O),
+  pinned against the Jacobian form), since a dequantized e4m3 V is in general
+  no bf16 value and a one-member subsequence would otherwise show the
+  rounding of O as a gradient that should be zero.  Every product of two
+  codes is exact (bf16 MFMA on the widened codes) and accumulates in fp32; P
+  and dS enter their products as bf16, as in the bf16 backward pass, so its
+  bar applies: max|g - g_ref| <= 2e-2 * max|g_ref| per tensor.
+* Chained (the kernels' own forward output and log-sum-exp feed the
+  backward): D = rowsum(dO * O) takes the 8-bit forward's output, whose P
+  went through e4m3, so the gradients inherit that forward's error; the bar is
+  the 8-bit forward's, 6e-2 of each tensor's largest entry.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fixed_pattern_sparse_amd as sk
+import workloads as wl
+from oracle import skiparse_bwd as bwd
+from oracle import skiparse_ref as ref
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = 2e-2
+TOL_CHAIN = 6e-2
+
+
+def score_magnitude(q, k, kf, mode, scale=None):
+    """M[b, token, head] = max over the keys j of the token's subsequence of
+    scale * sum_d |q_d| |k_jd| (float64, (B, T*H*W, heads))."""
+    B, T, H, W, nh, d = q.shape
+    N = T * H * W
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    qa = np.abs(q).reshape(B, N, nh, d)
+    ka = np.abs(k).reshape(B, N, nh, d)
+    out = np.zeros((B, N, nh))
+    for mem in ref.subsequence_members(T, H, W, kf, mode):
+        if mem.size == 0:
+            continue
+        for b in range(B):
+            for h in range(nh):
+                out[b, mem, h] = scale * (qa[b, mem, h] @ ka[b, mem, h].T).max(axis=1)
+    return out
+
+
+def np64(t):
+    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+
+
+def rel_err(got, want):
+    """max|got - want| / max|want|, the denominator floored at 1e-3 (a
+    gradient that is zero in exact arithmetic is held to 1e-3 of the bar)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert np.all(np.isfinite(got)), "non-finite gradient"
+    return float(np.max(np.abs(got - want))) / max(1e-3, float(np.max(np.abs(want))))
+
+
+def inputs(shp, seed, outliers=False):
+    xs = []
+    for i in range(4):
+        x = wl.normal_tensor(shp, seed, i)
+        if outliers and i < 3:
+            x = x * np.where(np.arange(shp[-1]) % 20 == 3, np.float32(8.0), np.float32(1.0))
+        xs.append(torch.from_numpy(x).to(torch.bfloat16))
+    return xs
+
+
+def quantize_gpu(q, k, v, do):
+    scales = torch.empty((3, 2), dtype=torch.float32, device=DEV)
+    codes = [sk.quantize_fp8(t.to(DEV), scale_out=scales[i])[0] for i, t in enumerate((q, k, v))]
+    dscale = torch.empty(2, dtype=torch.float32, device=DEV)
+    do8 = sk.quantize_fp8(do.to(DEV), scale_out=dscale)[0]
+    return codes, scales, do8, dscale
+
+
+SMALL = [
+    ((1, 3, 13, 22, 2, 128), 2, 0, False),
+    ((1, 3, 13, 22, 2, 128), 2, 1, True),
+    ((2, 2, 9, 17, 2, 128), 3, 1, False),
+    ((1, 2, 10, 10, 2, 128), 1, 0, True),     # k = 1: plain attention over 200 tokens
+    ((1, 5, 8, 40, 1, 128), 4, 0, False),
+    ((1, 1, 1, 1, 1, 128), 2, 0, False),      # one token: three empty subsequences
+    ((1, 2, 4, 16, 1, 128), 2, 1, False),     # 32-member subsequences: exact tiles
+    ((1, 2, 70, 66, 1, 128), 8, 0, False),    # k = 8: 64 subsequences, heavy padding
+]
+
+
+@pytest.mark.parametrize("shp,kf,mode,outl", SMALL)
+def test_fwd_lse_fp8_small(shp, kf, mode, outl):
+    q, k, v, _ = inputs(shp, 501, outl)
+    out, lse, codes, scales = sk.attention_train_fp8(q.to(DEV), k.to(DEV), v.to(DEV), kf, mode)
+    plain = sk.attention(*codes, kf, mode, descale_qkv=scales)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)
+    t = bwd.quantized_inputs(np64(q), np64(k), np64(v))
+    for name, c in zip("qkv", codes):
+        np.testing.assert_array_equal(c.cpu().numpy(), t[name + "8"])
+    want = bwd.attention_lse(t["q"], t["k"], kf, mode)
+    got = lse.cpu().numpy().astype(np.float64)
+    members = ref.subsequence_members(*shp[1:4], kf, mode)
+    real = np.concatenate([m for m in members if m.size])
+    bound = 2.0 ** -11 * score_magnitude(t["q"], t["k"], kf, mode) + 2.0 ** -12
+    err = np.abs(got - want)[:, real]
+    assert np.all(err <= bound[:, real]), float(np.max(err - bound[:, real]))
+
+
+@pytest.mark.parametrize("shp,kf,mode,outl", SMALL)
+def test_bwd_fp8_small(shp, kf, mode, outl):
+    q, k, v, do = inputs(shp, 502, outl)
+    t = bwd.quantized_inputs(np64(q), np64(k), np64(v), np64(do))
+    o_ref = ref.skiparse_attention(t["q"], t["k"], t["v"], kf, mode)
+    o_in = torch.from_numpy(o_ref.astype(np.float32)).to(torch.bfloat16)
+    dq_w, dk_w, dv_w, _ = bwd.skiparse_attention_bwd_fp8(np64(q), np64(k), np64(v), np64(do), kf, mode, o=np64(o_in))
+    lse_ref = bwd.attention_lse(t["q"], t["k"], kf, mode)
+    codes, scales, do8, dscale = quantize_gpu(q, k, v, do)
+    np.testing.assert_array_equal(do8.cpu().numpy(), t["do8"])
+    o_in = o_in.to(DEV)
+    lse_in = torch.from_numpy(lse_ref.astype(np.float32)).to(DEV)
+    plan = sk.skiparse_plan_init(*shp, kf, mode)
+    grads = [torch.empty(shp, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    sk.skiparse_attn_bwd_fp8(plan, *codes, scales, o_in, do8, dscale, lse_in, *grads)
+    torch.cuda.synchronize()
+    for name, g, w in zip(("dq", "dk", "dv"), grads, (dq_w, dk_w, dv_w)):
+        assert rel_err(np64(g), w) <= TOL, name
+
+
+@pytest.mark.parametrize("shp,kf,mode,outl", SMALL[:4])
+def test_train_fp8_chained_small(shp, kf, mode, outl):
+    q, k, v, do = inputs(shp, 503, outl)
+    out, lse, codes, scales = sk.attention_train_fp8(q.to(DEV), k.to(DEV), v.to(DEV), kf, mode)
+    dq, dk, dv = sk.attention_bwd_fp8(codes, scales, out, do.to(DEV), lse, kf, mode)
+    torch.cuda.synchronize()
+    want = bwd.skiparse_attention_bwd_fp8(np64(q), np64(k), np64(v), np64(do), kf, mode)[:3]
+    for name, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        assert rel_err(np64(g), w) <= TOL_CHAIN, name
+
+
+def test_bwd_fp8_deterministic_and_subsequence_ranges():
+    """Two calls agree bit for bit; runs over [0, 1) and [1, 4) give the full
+    call's gradients and leave rows outside their subsequences untouched."""
+    shp, kf, mode = (1, 2, 11, 14, 2, 128), 2, 0
+    q, k, v, do = inputs(shp, 504)
+    out, lse, codes, scales = sk.attention_train_fp8(q.to(DEV), k.to(DEV), v.to(DEV), kf, mode)
+    a = sk.attention_bwd_fp8(codes, scales, out, do.to(DEV), lse, kf, mode)
+    b = sk.attention_bwd_fp8(codes, scales, out, do.to(DEV), lse, kf, mode)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    _, _, do8, dscale = quantize_gpu(q, k, v, do)
+    plan = sk.skiparse_plan_init(*shp, kf, mode)
+    parts = [torch.full(shp, float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    sk.skiparse_attn_bwd_fp8(plan, *codes, scales, out, do8, dscale, lse, *parts, sub_begin=1, sub_count=3)
+    torch.cuda.synchronize()
+    members = ref.subsequence_members(*shp[1:4], kf, mode)
+    rows = lambda t: t.reshape(shp[0], -1, shp[4], shp[5])
+    for p in parts:
+        assert torch.isnan(rows(p)[:, members[0]].float()).all()
+    sk.skiparse_attn_bwd_fp8(plan, *codes, scales, out, do8, dscale, lse, *parts, sub_begin=0, sub_count=1)
+    torch.cuda.synchronize()
+    for p, f in zip(parts, a):
+        assert torch.equal(p, f)
+
+
+def sampled(members, rng, per_sub=6):
+    toks = []
+    for mem in members:
+        if mem.size:
+            toks += [mem[0], mem[-1]] + list(rng.choice(mem, size=min(per_sub, mem.size), replace=False))
+    return np.unique(np.array(toks, np.int64))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_train_fp8_workload_sampled(mode):
+    """The 8-bit training step at 720P-5s (k = 2): the kernels' forward feeds
+    the backward (chained bar), sampled rows against the oracle's gradients of
+    the dequantized tensors.  The oracle forms a head's dequantized rows alone
+    from the whole tensor's amax."""
+    w = wl.WORKLOADS["720p_5s"]
+    shp = w.shape
+    B, T, H, W, nh, d = shp
+    N = T * H * W
+    cpu = [torch.from_numpy(wl.normal_tensor(shp, w.seed + 20, i)).to(torch.bfloat16) for i in range(4)]
+    q, k, v, do = (t.to(DEV) for t in cpu)
+    out, lse, codes, scales = sk.attention_train_fp8(q, k, v, w.k, mode)
+    dq, dk, dv = sk.attention_bwd_fp8(codes, scales, out, do, lse, w.k, mode)
+    torch.cuda.synchronize()
+    xs = [t.float().numpy().reshape(B, N, nh, d) for t in cpu]
+    amax = [np.float32(np.max(np.abs(x))) for x in xs]
+    g = [t.float().cpu().numpy().reshape(B, N, nh, d) for t in (dq, dk, dv)]
+    members = ref.subsequence_members(T, H, W, w.k, mode)
+    rng = np.random.default_rng(w.seed + 20)
+    worst = [0.0, 0.0, 0.0]
+
+    def head(h):
+        return [bwd.dequantized_part(x[:, :, h:h + 1], a) for x, a in zip(xs, amax)]
+
+    for h in (0, nh - 1):
+        qh, kh, vh, doh = head(h)
+        toks = sampled(members, rng)
+        want = bwd.dq_rows(qh, kh, vh, doh, T, H, W, w.k, mode, 0, 0, toks)
+        worst[0] = max(worst[0], rel_err(g[0][0, toks, h], want))
+    h = nh // 2
+    qh, kh, vh, doh = head(h)
+    toks = sampled(members, rng)
+    wk, wv = bwd.dkv_rows(qh, kh, vh, doh, T, H, W, w.k, mode, 0, 0, toks)
+    worst[1] = rel_err(g[1][0, toks, h], wk)
+    worst[2] = rel_err(g[2][0, toks, h], wv)
+    assert max(worst) <= TOL_CHAIN, worst

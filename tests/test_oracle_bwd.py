@@ -157,3 +157,71 @@ def test_planted_mistakes_fail_finite_differences(mistake):
         np.testing.assert_allclose(ok[which].ravel(), fd, rtol=1e-6, atol=1e-8)   # the correct copy passes
         worst = max(worst, float(np.max(np.abs(bad[which].ravel() - fd))))
     assert worst > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# 8-bit training: quantize per tensor, then the gradients of the dequantized
+# tensors.  Inputs built on the e4m3 grid with amax 224 (Q, K, V) and 112 (dO)
+# have per-tensor scales 448 / 224 = 2 and 448 / 112 = 4 exactly in fp32 (the
+# 1e-12 of the rule is far below half an ulp of either amax), so quantization
+# is exact and the 8-bit gradients must equal the plain ones on the same
+# values; a path that forgot to dequantize, or scaled one tensor with
+# another's maximum, is off by a power of two.
+# ---------------------------------------------------------------------------
+
+def grid_tensor(shape, seed, amax, min_abs=0.0):
+    """Values code / (448 / amax) for random finite e4m3 codes, one of them 448;
+    with min_abs, codes below it in magnitude (other than zero) are left out."""
+    from oracle import fp8_ref as f8
+    table = f8.e4m3_decode_table()
+    finite = np.flatnonzero(np.isfinite(table) & ((np.abs(table) >= min_abs) | (table == 0)))
+    rng = np.random.default_rng(seed)
+    vals = table[rng.choice(finite, size=int(np.prod(shape)))].astype(np.float64)
+    vals[rng.integers(vals.size)] = 448.0
+    return (vals * (amax / 448.0)).reshape(shape)
+
+
+@pytest.mark.parametrize("shp,kf,mode", [((1, 2, 5, 6, 2, 8), 2, 0), ((1, 2, 9, 7, 1, 8), 3, 1)])
+def test_fp8_bwd_equals_plain_bwd_on_exact_grid(shp, kf, mode):
+    q, k, v = (grid_tensor(shp, 61 + i, 224.0) for i in range(3))
+    do = grid_tensor(shp, 64, 112.0)
+    dq, dk, dv, t = bwd.skiparse_attention_bwd_fp8(q, k, v, do, kf, mode)
+    assert (t["s_q"], t["s_k"], t["s_v"], t["s_do"]) == (2.0, 2.0, 2.0, 4.0)
+    for name, x in (("q", q), ("k", k), ("v", v), ("do", do)):
+        np.testing.assert_array_equal(t[name], x)
+    want = bwd.skiparse_attention_bwd(q, k, v, do, kf, mode)
+    for got, w in zip((dq, dk, dv), want):
+        np.testing.assert_array_equal(got, w)
+
+
+def test_fp8_gradient_maximum_applies_to_do_only():
+    shp = (1, 2, 5, 6, 1, 8)
+    q, k, v = (grid_tensor(shp, 71 + i, 224.0) for i in range(3))
+    # with maximum 224 the codes of dO are the grid values halved: normal
+    # values of at least 2^-5 stay exact when halved (e4m3's smallest normal
+    # is 2^-6)
+    do = grid_tensor(shp, 74, 112.0, min_abs=2.0 ** -5)
+    t = bwd.quantized_inputs(q, k, v, do, fp8_max=448.0, fp8_max_grad=224.0)
+    assert (t["s_q"], t["s_k"], t["s_v"], t["s_do"]) == (2.0, 2.0, 2.0, 2.0)
+    np.testing.assert_array_equal(t["do"], do)
+    q2 = grid_tensor(shp, 75, 224.0, min_abs=2.0 ** -5)
+    t2 = bwd.quantized_inputs(q2, k, v, do, fp8_max=224.0, fp8_max_grad=448.0)
+    assert (t2["s_q"], t2["s_do"]) == (1.0, 4.0)
+    np.testing.assert_array_equal(t2["q"], q2)
+
+
+@pytest.mark.parametrize("shp,kf,mode", [((1, 2, 5, 6, 2, 8), 2, 0), ((1, 1, 7, 7, 1, 4), 3, 1),
+                                         ((1, 1, 1, 1, 1, 8), 2, 0)])
+def test_bwd_with_given_output_equals_jacobian_form(shp, kf, mode):
+    """The row term from a given output, rowsum(dO * O), equals the Jacobian's
+    rowsum(P * dP) when O is the exact forward output (sum_j P_ij dO_i . v_j =
+    dO_i . sum_j P_ij v_j); with a perturbed O the gradients move."""
+    q, k, v, do = (rand(shp, 81, i) for i in range(4))
+    o = ref.skiparse_attention(q, k, v, kf, mode)
+    a = bwd.skiparse_attention_bwd(q, k, v, do, kf, mode)
+    b = bwd.skiparse_attention_bwd(q, k, v, do, kf, mode, o=o)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(y, x, rtol=0, atol=1e-12)
+    c = bwd.skiparse_attention_bwd(q, k, v, do, kf, mode, o=o * (1 + 1e-3))
+    assert np.max(np.abs(c[0] - a[0])) > 1e-6
+    np.testing.assert_array_equal(c[2], a[2])         # dV does not involve the row term
