@@ -123,3 +123,37 @@ def test_graph_fp8_block():
     y2 = torch.empty_like(x)
     replay_and_check(g, [y], [want], s,
                      lambda: sk.skiparse_block_fwd_fp8(plan, x2, w_codes, w_scales, y2, workspace=work))
+
+
+def test_graph_fp8_training_step():
+    """The 8-bit training step, one graph: quantization of Q, K, V, the e4m3
+    forward keeping the log-sum-exp, quantization of dO with the gradient
+    maximum, the backward pass on the codes."""
+    shp = (1, 2, 9, 17, 2, 128)
+    q, k, v, do = (bf16(shp, 1105, i) for i in range(4))
+    plan = sk.skiparse_plan_init(*shp, 2, sk.MODE_TOKEN)
+    B, T, H, W, nh, d = shp
+    codes = [torch.empty(shp, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    scales = torch.empty((3, 2), dtype=torch.float32, device=DEV)
+    dscale = torch.empty(2, dtype=torch.float32, device=DEV)
+    qws = torch.empty(sk.skiparse_quant_fp8_workspace_bytes(q.numel()), dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, T * H * W, nh), dtype=torch.float32, device=DEV)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    ws = torch.empty(sk.skiparse_attn_bwd_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+
+    def step(stream=None):
+        for i, t in enumerate((q, k, v)):
+            sk.skiparse_quant_fp8(t, codes[i], scales[i], workspace=qws, stream=stream)
+        sk.skiparse_attn_fwd_lse_fp8(plan, codes[0], codes[1], codes[2], scales, o, lse, stream=stream)
+        sk.skiparse_quant_fp8(do, codes[3], dscale, workspace=qws, stream=stream)
+        sk.skiparse_attn_bwd_fp8(plan, codes[0], codes[1], codes[2], scales, o, codes[3], dscale, lse, *grads,
+                                 workspace=ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    outs = [o, lse, scales, dscale] + codes + grads
+    want = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    g = capture(lambda: step(s), s)
+    replay_and_check(g, outs, want, s, lambda: sk.attention_train_fp8(v, k, q, 2, sk.MODE_GROUP))
