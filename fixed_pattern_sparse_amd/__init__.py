@@ -554,12 +554,33 @@ def _autograd_function():
             dq, dk, dv = attention_bwd(q, k, v, out, dout, lse, ctx.kf, ctx.mode)
             return dq, dk, dv, None, None
 
-    return SkiparseAttention
+    class SkiparseAttentionFP8(torch.autograd.Function):
+        """8-bit training op: ``SkiparseAttentionFP8.apply(q, k, v, kf, mode)``
+        on bf16 device tensors.  The forward quantizes Q, K, V per tensor and
+        keeps only their e4m3 codes (half the bytes of bf16) with the output
+        and log-sum-exp; the backward quantizes dO per tensor and returns the
+        bf16 gradients of the dequantized tensors."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, kf, mode):
+            out, lse, codes, scales = attention_train_fp8(q, k, v, kf, mode)
+            ctx.save_for_backward(*codes, scales, out, lse)
+            ctx.kf, ctx.mode = kf, mode
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q8, k8, v8, scales, out, lse = ctx.saved_tensors
+            dq, dk, dv = attention_bwd_fp8((q8, k8, v8), scales, out, dout, lse, ctx.kf, ctx.mode)
+            return dq, dk, dv, None, None
+
+    return SkiparseAttention, SkiparseAttentionFP8
 
 
 def __getattr__(name):
-    if name == "SkiparseAttention":
-        cls = _autograd_function()
-        globals()[name] = cls
-        return cls
+    if name in ("SkiparseAttention", "SkiparseAttentionFP8"):
+        a, b = _autograd_function()
+        globals()["SkiparseAttention"] = a
+        globals()["SkiparseAttentionFP8"] = b
+        return globals()[name]
     raise AttributeError(name)

@@ -227,3 +227,19 @@ def test_train_fp8_workload_sampled(mode):
     worst[1] = rel_err(g[1][0, toks, h], wk)
     worst[2] = rel_err(g[2][0, toks, h], wv)
     assert max(worst) <= TOL_CHAIN, worst
+
+
+def test_autograd_fp8_matches_the_calls():
+    """SkiparseAttentionFP8 gives the forward output and gradients of the two
+    8-bit calls bit for bit."""
+    shp, kf, mode = (1, 3, 13, 22, 2, 128), 2, 1
+    q, k, v, do = (t.to(DEV) for t in inputs(shp, 505))
+    out, lse, codes, scales = sk.attention_train_fp8(q, k, v, kf, mode)
+    grads = sk.attention_bwd_fp8(codes, scales, out, do, lse, kf, mode)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o2 = sk.SkiparseAttentionFP8.apply(qa, ka, va, kf, mode)
+    o2.backward(do)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.detach(), out)
+    for g, a in zip(grads, (qa.grad, ka.grad, va.grad)):
+        assert torch.equal(g, a)
