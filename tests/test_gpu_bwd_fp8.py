@@ -243,3 +243,25 @@ def test_autograd_fp8_matches_the_calls():
     assert torch.equal(o2.detach(), out)
     for g, a in zip(grads, (qa.grad, ka.grad, va.grad)):
         assert torch.equal(g, a)
+
+
+def test_train_fp8_index_function_path():
+    """n = 24200 members exceeds the token-table capacity: the dQ kernel takes
+    rows from the index function (chained bar, sampled rows)."""
+    shp, kf, mode = (1, 1, 22, 1100, 1, 128), 1, 0
+    B, T, H, W, nh, d = shp
+    N = T * H * W
+    cpu = [torch.from_numpy(wl.normal_tensor(shp, 506, i)).to(torch.bfloat16) for i in range(4)]
+    q, k, v, do = (t.to(DEV) for t in cpu)
+    out, lse, codes, scales = sk.attention_train_fp8(q, k, v, kf, mode)
+    grads = sk.attention_bwd_fp8(codes, scales, out, do, lse, kf, mode)
+    torch.cuda.synchronize()
+    xs = [t.float().numpy().reshape(B, N, nh, d) for t in cpu]
+    deq = [bwd.dequantized_part(x, np.float32(np.max(np.abs(x)))) for x in xs]
+    g = [t.float().cpu().numpy().reshape(B, N, nh, d) for t in grads]
+    members = ref.subsequence_members(T, H, W, kf, mode)
+    toks = sampled(members, np.random.default_rng(506), per_sub=24)
+    want_q = bwd.dq_rows(*deq, T, H, W, kf, mode, 0, 0, toks)
+    want_k, want_v = bwd.dkv_rows(*deq, T, H, W, kf, mode, 0, 0, toks)
+    worst = [rel_err(g[0][0, toks, 0], want_q), rel_err(g[1][0, toks, 0], want_k), rel_err(g[2][0, toks, 0], want_v)]
+    assert max(worst) <= TOL_CHAIN, worst
