@@ -1,0 +1,67 @@
+"""The bf16 forward past the 32-bit offset limits.  A (1, 1, 4096, 4096, 1,
+128) tensor has 2^24 tokens and 4 GiB per batch sample, so the kernels find
+rows through the index function with 64-bit offsets.  At k = 8 the 64
+subsequences hold 262,144 tokens each.  The inputs come from the counter-based
+generator of the workloads module (drawn on the device; the oracle forms only
+the rows it needs on the host), with Q and K scaled by 8 so that each query's
+softmax is peaked and its output depends on which key rows were read.  Sampled
+rows of three subsequences (the first, a middle one, the last, which holds the
+tensor's last token) against the oracle at the bf16 bar."""
+
+import numpy as np
+import pytest
+import torch
+
+import fixed_pattern_sparse_amd as sk
+import workloads as wl
+from oracle import skiparse_ref as ref
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = (1, 1, 4096, 4096, 1, 128)
+KF = 8
+GAIN = (8.0, 8.0, 1.0)          # Q, K, V
+TOL = 2e-2
+
+
+class HashRows:
+    """The (B, N, heads, d) view of a hash tensor that the oracle indexes with
+    [b, token indices, head]; rows are formed on demand."""
+
+    def __init__(self, tensor_id, gain):
+        B, T, H, W, nh, d = SHAPE
+        self.shape = (B, T * H * W, nh, d)
+        self.t, self.gain = tensor_id, gain
+
+    def __getitem__(self, key):
+        b, idx, h = key
+        B, N, nh, d = self.shape
+        idx = np.asarray(idx, np.int64)
+        flat = ((b * N + idx)[:, None] * nh + h) * d + np.arange(d)[None, :]
+        return wl.hash_values(self.t, flat, self.gain)
+
+
+@pytest.mark.parametrize("mode", [sk.MODE_TOKEN, sk.MODE_GROUP])
+def test_bf16_past_32bit_offsets(mode):
+    B, T, H, W, nh, d = SHAPE
+    N = T * H * W
+    assert N >= 1 << 24 and N * nh * d * 2 >= 1 << 32
+    q, k, v = (wl.hash_fill_(torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda"), i, GAIN[i])
+               for i in range(3))
+    o = sk.attention(q, k, v, KF, mode)
+    torch.cuda.synchronize()
+    members = ref.subsequence_members(T, H, W, KF, mode)
+    rng = np.random.default_rng(7)
+    toks = []
+    for s in (0, len(members) // 2, len(members) - 1):
+        mem = members[s]
+        toks += [int(mem[0]), int(mem[-1])] + [int(x) for x in rng.choice(mem, 2, replace=False)]
+    toks = np.array(sorted(set(toks)), np.int64)
+    assert toks[-1] == N - 1                            # the tensor's last token is sampled
+    got = o.view(B, N, nh, d)[0, torch.from_numpy(toks).cuda(), 0].float().cpu().numpy().astype(np.float64)
+    del q, k, v, o
+    qs, ks, vs = (HashRows(i, GAIN[i]) for i in range(3))
+    want = ref.attention_rows(qs, ks, vs, T, H, W, KF, mode, 0, 0, toks)
+    assert np.max(np.abs(want)) > 0.05                 # peaked softmax: the rows carry V's values
+    err = np.max(np.abs(got - want)) / max(1.0, np.max(np.abs(want)))
+    assert err <= TOL, err

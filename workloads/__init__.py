@@ -126,3 +126,41 @@ def make_inputs(w: Workload, workers: int | None = None):
         out.append(t)
         del x
     return tuple(out)
+
+
+# ---------------------------------------------------------------------------
+# Counter-based values for tensors too large to draw on the host: element i of
+# tensor t is ((i * 2654435761 + t * 40503) mod 2^32 >> 8) / 2^24 - 0.5, times
+# a power-of-two gain, computed in fp32 (exact) and rounded to bf16 (nearest
+# even).  Both generators below follow this definition, one in numpy for any
+# set of indices, one with torch integer ops on the device for a whole tensor.
+# ---------------------------------------------------------------------------
+
+HASH_MUL = 2654435761
+HASH_TENSOR = 40503
+
+
+def hash_values(tensor_id: int, idx, gain: float = 1.0) -> np.ndarray:
+    """float32 values (already on the bf16 grid) of the elements at flat
+    indices ``idx`` (any integer array)."""
+    import torch
+    i = np.asarray(idx, np.uint64)
+    h = (i * np.uint64(HASH_MUL) + np.uint64(tensor_id * HASH_TENSOR)) & np.uint64(0xFFFFFFFF)
+    v = (h >> np.uint64(8)).astype(np.float32) / np.float32(16777216.0) - np.float32(0.5)
+    v = v * np.float32(gain)
+    return torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).float().numpy()
+
+
+def hash_fill_(t, tensor_id: int, gain: float = 1.0, chunk: int = 1 << 27):
+    """Fill the bf16 device tensor ``t`` (contiguous) with the values of
+    :func:`hash_values` for its flat indices, in chunks."""
+    import torch
+    flat = t.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        i = torch.arange(s, e, dtype=torch.int64, device=t.device)
+        h = (i * HASH_MUL + tensor_id * HASH_TENSOR) & 0xFFFFFFFF
+        v = (h >> 8).to(torch.float32) / 16777216.0 - 0.5
+        flat[s:e] = (v * gain).to(torch.bfloat16)
+    return t
