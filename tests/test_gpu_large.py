@@ -65,3 +65,71 @@ def test_bf16_past_32bit_offsets(mode):
     assert np.max(np.abs(want)) > 0.05                 # peaked softmax: the rows carry V's values
     err = np.max(np.abs(got - want)) / max(1.0, np.max(np.abs(want)))
     assert err <= TOL, err
+
+
+def exact_amax_index(tensor_id, n):
+    """An element index below n whose hash is below 256 (value exactly -0.5
+    times the gain, the largest magnitude the generator makes), found by
+    solving i * HASH_MUL + t * HASH_TENSOR = r (mod 2^32) for r = 0, 1, ...;
+    None if there is none below 2^14 tries."""
+    inv = pow(wl.HASH_MUL, -1, 1 << 32)
+    c = tensor_id * wl.HASH_TENSOR
+    for r in range(1 << 14):
+        i = ((r - c) * inv) % (1 << 32)
+        if i < n and ((i * wl.HASH_MUL + c) % (1 << 32)) < 256:
+            return i
+    return None
+
+
+class DequantRows(HashRows):
+    """Rows of a hash tensor after per-tensor e4m3 quantization with the
+    oracle's codec at the scale 448 / (amax + 1e-12), amax = 0.5 * gain."""
+
+    def __init__(self, tensor_id, gain):
+        super().__init__(tensor_id, gain)
+        from oracle import fp8_ref as f8
+        self.f8 = f8
+        self.scale = f8.per_tensor_scale(np.float32(0.5 * gain))
+
+    def __getitem__(self, key):
+        v = super().__getitem__(key)
+        codes = self.f8.e4m3_encode((v * self.scale).astype(np.float32))
+        return self.f8.dequantize(codes, self.scale)
+
+
+def test_fp8_past_32bit_offsets():
+    """Per-tensor quantization over 2^31 elements and the e4m3 forward on the
+    64-bit path, token-wise, at the fp8 bar."""
+    mode = sk.MODE_TOKEN
+    B, T, H, W, nh, d = SHAPE
+    N = T * H * W
+    numel = N * nh * d
+    assert numel >= 1 << 31
+    for i in range(3):                                   # amax = 0.5 * gain exactly
+        assert exact_amax_index(i, numel) is not None
+    q, k, v = (wl.hash_fill_(torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda"), i, GAIN[i])
+               for i in range(3))
+    o, codes, scales = sk.attention_fp8(q, k, v, KF, mode)
+    torch.cuda.synchronize()
+    dq = [DequantRows(i, GAIN[i]) for i in range(3)]
+    got_scales = scales.cpu().numpy()
+    for i in range(3):
+        assert got_scales[i, 0] == dq[i].scale, (i, got_scales[i], dq[i].scale)
+    members = ref.subsequence_members(T, H, W, KF, mode)
+    rng = np.random.default_rng(8)
+    toks = []
+    for s in (0, len(members) // 2, len(members) - 1):
+        mem = members[s]
+        toks += [int(mem[0]), int(mem[-1])] + [int(x) for x in rng.choice(mem, 2, replace=False)]
+    toks = np.array(sorted(set(toks)), np.int64)
+    assert toks[-1] == N - 1
+    sel = torch.from_numpy(toks).cuda()
+    got = o.view(B, N, nh, d)[0, sel, 0].float().cpu().numpy().astype(np.float64)
+    got_codes = codes[2].view(B, N, nh, d)[0, sel, 0].cpu().numpy()
+    del q, k, v, o, codes
+    want_codes = dq[2].f8.e4m3_encode((HashRows(2, GAIN[2])[0, toks, 0] * dq[2].scale).astype(np.float32))
+    np.testing.assert_array_equal(got_codes, want_codes)    # V's codes at the sampled rows, bit for bit
+    want = ref.attention_rows(*dq, T, H, W, KF, mode, 0, 0, toks)
+    assert np.max(np.abs(want)) > 0.05
+    err = np.max(np.abs(got - want)) / max(1.0, np.max(np.abs(want)))
+    assert err <= 6e-2, err
