@@ -104,8 +104,8 @@ def main():
                          "one group-wise layer, no timing")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path; "
-              "the sharding design is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no multi-GPU path; "
+              "a rank would run its share of the subsequences through sub_begin / sub_count", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -278,7 +278,7 @@ int skiparse_attn_fwd(const skiparse_plan* plan, skiparse_dtype dtype, const voi
     case SKIPARSE_BF16: e = launch_attn_bf16(a, plan->B, d, stream); break;
     default: e = launch_attn_fp8(a, plan->B, d, stream); break;
   }
-  if (e == hipErrorNotSupported) return fail(SKIPARSE_EUNSUPPORTED, "this dtype has no kernel in this build");
+  if (e == hipErrorNotSupported) return fail(SKIPARSE_EUNSUPPORTED, "this dtype has no kernel in the library");
   if (e != hipSuccess) return fail(SKIPARSE_EHIP, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -367,7 +367,7 @@ int skiparse_attn_bwd(const skiparse_plan* plan, skiparse_dtype dtype, const voi
   a.dv = dv;
   (void)hipGetLastError();
   const hipError_t e = launch_attn_bwd(a, plan->B, d, stream);
-  if (e == hipErrorNotSupported) return fail(SKIPARSE_EUNSUPPORTED, "this head dim has no backward kernel in this build");
+  if (e == hipErrorNotSupported) return fail(SKIPARSE_EUNSUPPORTED, "this head dim has no backward kernel in the library");
   if (e != hipSuccess) return fail(SKIPARSE_EHIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -1,5 +1,5 @@
 """bench.py's command line on the CPU: more than one GPU is refused with a
-message (this build runs on one GPU), before anything touches a device."""
+message (the benchmark runs on one GPU), before anything touches a device."""
 
 import os
 import subprocess
