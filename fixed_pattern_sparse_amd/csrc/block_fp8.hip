@@ -11,7 +11,10 @@
 // Rotary embedding: head dimension d cut into (d_t, d_h, d_w); inside the part
 // of axis a, pair (x_2i, x_2i+1) (i counted from the part's start) turns by
 // pos_a * theta^(-2i / d_a), pos_a the token's t, h or w.  The cos/sin of every
-// (axis, position, pair) come from a table the first kernel fills in float64.
+// (axis, position, pair) come from a table the first kernel fills in float64;
+// when it fits (kTabCap entries), each work-group of the two streaming kernels
+// copies it to LDS first, so the four lookups per 16-byte vector are LDS
+// reads rather than dependent global loads.
 #include <cmath>
 
 #include "fp8_codec.h"
@@ -22,6 +25,7 @@ namespace {
 
 constexpr int kThreads = kQuantThreads;
 constexpr int kMaxBlocks = 2048;
+constexpr int kTabCap = 4096;   // table entries staged in LDS (32 KB)
 
 __global__ void rope_table_kernel(RopeGeom r, double log_theta, float2* __restrict__ tab) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -45,8 +49,7 @@ __global__ void rope_table_kernel(RopeGeom r, double log_theta, float2* __restri
 
 // cos/sin of the pair that starts at even head-dim index e of a token at
 // (t, h, w).
-__device__ __forceinline__ float2 rope_cs(const RopeGeom& r, const float2* __restrict__ tab, int e, int t, int h,
-                                          int w) {
+__device__ __forceinline__ float2 rope_cs(const RopeGeom& r, const float2* tab, int e, int t, int h, int w) {
   const int p = e >> 1;
   if (e < r.dt) return tab[t * (r.dt >> 1) + p];
   if (e < r.dt + r.dh) return tab[r.tab_h + h * (r.dh >> 1) + (p - (r.dt >> 1))];
@@ -54,8 +57,7 @@ __device__ __forceinline__ float2 rope_cs(const RopeGeom& r, const float2* __res
 }
 
 // Rotate the 8 bf16 values of vector i (token tok, head-dim offset e0) into v[8].
-__device__ __forceinline__ void rope8(const RopeGeom& r, const float2* __restrict__ tab, uint4 u, uint32_t i,
-                                      float v[8]) {
+__device__ __forceinline__ void rope8(const RopeGeom& r, const float2* tab, uint4 u, uint32_t i, float v[8]) {
   const uint32_t tok = fdiv(i, r.div_cv);
   const uint32_t e0 = (i - tok * r.div_cv.d) * 8u;
   const uint32_t e = e0 & (uint32_t)(r.d - 1);          // d is a power of two
@@ -75,8 +77,24 @@ __device__ __forceinline__ void rope8(const RopeGeom& r, const float2* __restric
   }
 }
 
-__global__ void __launch_bounds__(kThreads) rope_amax_kernel(RopeGeom r, const float2* __restrict__ tab,
+// The table as the streaming loop reads it: staged in LDS (LDS_TAB) or global.
+template <bool LDS_TAB>
+__device__ __forceinline__ const float2* rope_table(const RopeGeom& r, const float2* __restrict__ tab,
+                                                    float2* stage) {
+  if constexpr (LDS_TAB) {
+    for (int k = threadIdx.x; k < r.tab_len; k += kThreads) stage[k] = tab[k];
+    __syncthreads();
+    return stage;
+  } else {
+    return tab;
+  }
+}
+
+template <bool LDS_TAB>
+__global__ void __launch_bounds__(kThreads) rope_amax_kernel(RopeGeom r, const float2* __restrict__ gtab,
                                                              const uint4* __restrict__ x, float* __restrict__ part) {
+  __shared__ float2 stage[LDS_TAB ? kTabCap : 1];
+  const float2* tab = rope_table<LDS_TAB>(r, gtab, stage);
   float m = 0.f;
   for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < r.nvec; i += gridDim.x * kThreads) {
     float v[8];
@@ -88,10 +106,13 @@ __global__ void __launch_bounds__(kThreads) rope_amax_kernel(RopeGeom r, const f
   if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
-__global__ void __launch_bounds__(kThreads) rope_encode_kernel(RopeGeom r, const float2* __restrict__ tab,
+template <bool LDS_TAB>
+__global__ void __launch_bounds__(kThreads) rope_encode_kernel(RopeGeom r, const float2* __restrict__ gtab,
                                                                const uint4* __restrict__ x,
                                                                const float* __restrict__ scale,
                                                                uint2* __restrict__ y) {
+  __shared__ float2 stage[LDS_TAB ? kTabCap : 1];
+  const float2* tab = rope_table<LDS_TAB>(r, gtab, stage);
   const float s = scale[0];
   for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < r.nvec; i += gridDim.x * kThreads) {
     float v[8];
@@ -118,13 +139,21 @@ hipError_t launch_rope_table(const RopeGeom& r, float theta, float2* tab, hipStr
 hipError_t launch_rope_quant(const RopeGeom& r, const float2* tab, const void* x, uint8_t* y, float* scale,
                              float* part, hipStream_t stream) {
   const int nb = rope_blocks(r.nvec);
-  hipLaunchKernelGGL(rope_amax_kernel, dim3(nb), dim3(kThreads), 0, stream, r, tab, (const uint4*)x, part);
+  const bool lds = r.tab_len <= kTabCap;
+  if (lds)
+    hipLaunchKernelGGL(rope_amax_kernel<true>, dim3(nb), dim3(kThreads), 0, stream, r, tab, (const uint4*)x, part);
+  else
+    hipLaunchKernelGGL(rope_amax_kernel<false>, dim3(nb), dim3(kThreads), 0, stream, r, tab, (const uint4*)x, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_fp8_scale(part, nb, kE4M3Max, 1e-12f, scale, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rope_encode_kernel, dim3(nb), dim3(kThreads), 0, stream, r, tab, (const uint4*)x, scale,
-                     (uint2*)y);
+  if (lds)
+    hipLaunchKernelGGL(rope_encode_kernel<true>, dim3(nb), dim3(kThreads), 0, stream, r, tab, (const uint4*)x, scale,
+                       (uint2*)y);
+  else
+    hipLaunchKernelGGL(rope_encode_kernel<false>, dim3(nb), dim3(kThreads), 0, stream, r, tab, (const uint4*)x,
+                       scale, (uint2*)y);
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ ROPE_CASES = [
     ((1, 2, 3, 4, 2, 128), 10000.0, (128, 0, 0)),
     ((1, 1, 1, 1, 1, 128), 10000.0, None),
     ((1, 21, 45, 80, 2, 128), 10000.0, None),
+    ((1, 2, 16, 200, 1, 128), 10000.0, None),    # table of 4580 entries: read from global memory, not LDS
 ]
 
 
