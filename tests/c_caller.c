@@ -7,6 +7,10 @@
  *                  (tensor t, element i): ((i * 2654435761 + t * 40503) mod 2^32
  *                  >> 8) / 2^24 - 0.5, exact in fp32 and bf16-rounded (nearest
  *                  even); writes the bf16 output to out.bin
+ *   c_caller attn8 B T H W heads d k mode out.bin
+ *                  the same inputs quantized per tensor to e4m3 on the
+ *                  device (skiparse_quant_fp8, maximum 448), then the e4m3
+ *                  forward; writes the bf16 output to out.bin
  *
  * Prints "error <code> <message>" and exits 1 on a library error.
  */
@@ -39,7 +43,7 @@ static float input_value(int t, uint64_t i) {
 
 int main(int argc, char** argv) {
   if (argc < 10) {
-    fprintf(stderr, "usage: c_caller plan|attn B T H W heads d k mode [out.bin]\n");
+    fprintf(stderr, "usage: c_caller plan|attn|attn8 B T H W heads d k mode [out.bin]\n");
     return 2;
   }
   int v[8];
@@ -65,7 +69,8 @@ int main(int argc, char** argv) {
     printf("bad %d %s\n", bad, skiparse_last_error()[0] ? "message" : "none");
     return 0;
   }
-  if (strcmp(argv[1], "attn") == 0 && argc >= 11) {
+  const int fp8 = strcmp(argv[1], "attn8") == 0;
+  if ((strcmp(argv[1], "attn") == 0 || fp8) && argc >= 11) {
     const size_t numel = (size_t)v[0] * v[1] * v[2] * v[3] * v[4] * v[5];
     uint16_t* host = (uint16_t*)malloc(numel * 2);
     void* dev[4];
@@ -82,7 +87,35 @@ int main(int argc, char** argv) {
         return 1;
       }
     }
-    check(skiparse_attn_fwd(&p, SKIPARSE_BF16, dev[0], dev[1], dev[2], dev[3], 0.0f, NULL, 0, 0, NULL));
+    if (fp8) {
+      void* codes[3];
+      float* scales = NULL;
+      void* ws = NULL;
+      const size_t wsb = skiparse_quant_fp8_workspace_bytes((int64_t)numel);
+      if (hipMalloc((void**)&scales, 6 * sizeof(float)) != hipSuccess || hipMalloc(&ws, wsb) != hipSuccess) {
+        printf("error hipMalloc\n");
+        return 1;
+      }
+      for (int t = 0; t < 3; ++t) {
+        if (hipMalloc(&codes[t], numel) != hipSuccess) {
+          printf("error hipMalloc\n");
+          return 1;
+        }
+        check(skiparse_quant_fp8(dev[t], SKIPARSE_BF16, (int64_t)numel, (uint8_t*)codes[t], scales + 2 * t, 448.0f,
+                                 1e-12f, ws, wsb, NULL));
+      }
+      check(skiparse_attn_fwd(&p, SKIPARSE_FP8_E4M3, codes[0], codes[1], codes[2], dev[3], 0.0f, scales, 0, 0,
+                              NULL));
+      if (hipDeviceSynchronize() != hipSuccess) {
+        printf("error hip\n");
+        return 1;
+      }
+      for (int t = 0; t < 3; ++t) hipFree(codes[t]);
+      hipFree(scales);
+      hipFree(ws);
+    } else {
+      check(skiparse_attn_fwd(&p, SKIPARSE_BF16, dev[0], dev[1], dev[2], dev[3], 0.0f, NULL, 0, 0, NULL));
+    }
     if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(host, dev[3], numel * 2, hipMemcpyDeviceToHost) != hipSuccess) {
       printf("error hip\n");
       return 1;

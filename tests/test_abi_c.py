@@ -1,7 +1,8 @@
 """The C ABI from a plain C program (tests/c_caller.c, built next to the
 library by the package build): the host plan and gather map against the
-oracle, bit-exact, and error reporting (CPU); the bf16 forward on the device
-from C against the oracle (GPU)."""
+oracle, bit-exact, and error reporting (CPU); the bf16 forward, and the
+per-tensor e4m3 quantization followed by the e4m3 forward, on the device from
+C against the oracle (GPU)."""
 
 import os
 import subprocess
@@ -60,3 +61,23 @@ def test_c_attention_on_device(mode, tmp_path):
                for t in range(3))
     want = ref.skiparse_attention(q, k, v, 2, mode)
     assert np.max(np.abs(got - want)) <= 2e-2 * max(1.0, np.max(np.abs(want)))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", [ref.TOKEN, ref.GROUP])
+def test_c_fp8_attention_on_device(mode, tmp_path):
+    import torch
+    from oracle import fp8_ref as f8
+    shp = (1, 2, 6, 10, 2, 128)
+    out_path = tmp_path / "o8.bin"
+    lines = caller("attn8", *shp, 2, mode, out_path)
+    assert lines[-1].startswith("attn ok")
+    got = torch.from_numpy(np.fromfile(out_path, dtype=np.uint16).astype(np.int16)).view(torch.bfloat16)
+    got = got.float().numpy().astype(np.float64).reshape(shp)
+    deq = []
+    for t in range(3):
+        x = torch.from_numpy(hash_inputs(shp, t)).to(torch.bfloat16).float().numpy()
+        codes, scale, _ = f8.quantize_per_tensor(x.reshape(-1))
+        deq.append(f8.dequantize(codes, scale).reshape(shp))
+    want = ref.skiparse_attention(*deq, 2, mode)
+    assert np.max(np.abs(got - want)) <= 6e-2 * max(1.0, np.max(np.abs(want)))
