@@ -404,8 +404,28 @@ def main():
                                            "attention_tflop": round(pl.flops / 1e12, 3),
                                            "projection_tflop": round(4 * 2 * M4 * C4 * C4 / 1e12, 3)}
             del y4, bf
+        del x4
+        # the same block (C = 1536) on the 720P-5s token grid, token-wise
+        T7, H7, W7 = 21, 45, 80
+        M7 = T7 * H7 * W7
+        x7 = torch.from_numpy(wl.normal_tensor((1, T7, H7, W7, C4), w4.seed, 9)).to(torch.bfloat16).cuda()
+        pl = sk.skiparse_plan_init(1, T7, H7, W7, nh4, d4, 2, sk.MODE_TOKEN)
+        bf = sk.BlockFP8(w_codes, w_scales, nh4, 2, sk.MODE_TOKEN)
+        y7 = bf(x7)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(5):
+            bf(x7, out=y7)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = e[0].elapsed_time(e[1]) / 5
+        flops = pl.flops + 4 * 2 * M7 * C4 * C4
+        block["block_720p_grid_12_heads_token"] = {"ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                                                   "attention_tflop": round(pl.flops / 1e12, 3),
+                                                   "projection_tflop": round(4 * 2 * M7 * C4 * C4 / 1e12, 3)}
+        del x7, y7, bf
         extras["block_fp8"] = block
-        del x4, w_codes, w_scales
+        del w_codes, w_scales
     result["extras"] = extras
 
     if not args.no_cpu_baseline:

@@ -264,6 +264,38 @@ def test_block_480p_sampled():
     assert torch.equal(y2.float(), 2.0 * y1.float())
 
 
+def test_block_720p_tokens_12_heads_sampled():
+    """The 720P-5s token grid (21 x 45 x 80 tokens, H padded to 48) with 12
+    heads of 128 (C = 1536), k = 2 token-wise: sampled rows of two
+    subsequences against the exact block, the 480p bars, and exact doubling
+    with Wo's scale halved."""
+    T, H, W, heads, d = 21, 45, 80, 12, 128
+    C = heads * d
+    codes, scales, deq, _ = weights(C, 821)
+    x, x64 = bf16_input((1, T, H, W, C), 822, 0)
+    xd = x.to(DEV)
+    blockf = sk.BlockFP8(codes, scales, heads, 2, ref.TOKEN)
+    y1 = blockf(xd)
+    torch.cuda.synchronize()
+    yh = y1.float().cpu().numpy().reshape(T * H * W, C)
+    assert np.all(np.isfinite(yh))
+    rng = np.random.Generator(np.random.PCG64(823))
+    members, _ = ref._members_for((T, H, W, 2, ref.TOKEN))
+    tokens = np.sort(np.concatenate([[members[3][-1]], rng.choice(members[0], size=12, replace=False),
+                                     rng.choice(members[3], size=11, replace=False)]))
+    tokens = np.unique(tokens)
+    want = exact_block_rows(x64, deq, heads, 2, ref.TOKEN, tokens)
+    r, m = rms_err(yh[tokens], want), max_err(yh[tokens], want)
+    print(f"720p-token block (12 heads) sampled rows vs exact: rms {r:.4f} max {m:.4f}")
+    assert r <= 0.1 and m <= 0.15
+    scales2 = scales.clone()
+    scales2[3, 1] *= 2.0
+    blockf.w_scales = scales2
+    y2 = blockf(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.float(), 2.0 * y1.float())
+
+
 @pytest.mark.skip(reason="the block's first version, with its projections on hipBLASLt, faulted the GPU at this "
                          "shape; no mistake in the block's own kernels was found by reading them (their indexing "
                          "is checked on the CPU at this shape), the projections now run on the library's own GEMM, "
