@@ -1,4 +1,4 @@
-"""A seeded sweep over small random shapes: every pattern (token-wise,
+"""A seeded sweep over 64 small random shapes: every pattern (token-wise,
 group-wise, and the two Skiparse-1D rules), k from 1 to 8, ragged H and W
 (padding, subsequences of one member or none), one to three heads, batch 1 or
 2.  Each case is compared element by element with the oracle on four paths,
@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def make_cases(n=24, seed=2024):
+def make_cases(n=64, seed=2024):
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
