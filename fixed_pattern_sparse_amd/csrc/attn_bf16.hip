@@ -68,11 +68,13 @@ struct Layout {
   __device__ static int vswz(int r) { return D == 128 ? ((r & 3) << 2) : ((r & 1) << 2); }
 };
 
-// ROWS selects where a key row's token comes from.  2: a table of the whole
-// subsequence's tokens, written once per work-group (n <= kTokCap); 1: a
-// walker over the (t, h') row and w' column tables (table room needed); both
-// use 32-bit offsets from a scalar base (T*H*W < 2^24, heads*d*2 < 2^24, a
-// batch sample's tensor < 4 GB).  0: the index function per row.
+// ROWS selects where a key row's token comes from.  3: the token is the
+// member index (stride 1 on both axes: k = 1, the whole grid in its own
+// order); 2: a table of the whole subsequence's tokens, written once per
+// work-group (n <= kTokCap); 1: a walker over the (t, h') row and w' column
+// tables (table room needed); these use 32-bit offsets from a scalar base
+// (T*H*W < 2^24, heads*d*2 < 2^24, a batch sample's tensor < 4 GB).  0: the
+// index function per row.
 template <int D, int ROWS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const AttnArgs a) {
@@ -121,10 +123,11 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < L::CPT; ++i) {
       int tok;
-      if constexpr (ROWS == 2) {
+      if constexpr (ROWS == 2 || ROWS == 3) {
         int jr = tile * kBN + tid / L::CH + i * L::RSTEP;
         jr = jr < n ? jr : n - 1;
-        tok = gTok[jr];
+        if constexpr (ROWS == 2) tok = gTok[jr];
+        else tok = jr;
         const uint32_t off = __umul24((uint32_t)tok, rsb) + (uint32_t)(lslot * 16);
         sgd.k[i] = *(const uint4*)(kb + off);
         sgd.v[i] = *(const uint4*)(vb + off);
@@ -356,7 +359,9 @@ hipError_t launch_d(AttnArgs a, int B, hipStream_t stream) {
   assign_tiles(a, B, kBM);
   if (a.total_tiles == 0) return hipSuccess;
   const int64_t row_bytes = (int64_t)a.row_stride * 2;
-  if (token_table_ok(a, row_bytes, kTokCap))
+  if (a.g.kh == 1 && a.g.kw == 1 && offsets32_ok(a, row_bytes))
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 3>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+  else if (token_table_ok(a, row_bytes, kTokCap))
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
   else if (fast_rows_ok(a, row_bytes))
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
