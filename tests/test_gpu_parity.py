@@ -233,13 +233,14 @@ def test_bf16_workload_sampled(name, kf, mode):
 
 
 @pytest.mark.parametrize("shp,kf,mode", [
-    ((1, 1, 24, 1100, 1, 64), 1, 0),   # n = 26400 over the token-table cap, 1100 columns: index function per row
-    ((1, 2, 60, 220, 1, 64), 1, 0),    # n = 26400 over the cap, row/column tables fit: table walker
+    ((1, 1, 48, 2200, 1, 64), 2, 0),   # n = 26400 over the token-table cap, 1100 local columns: index function per row
+    ((1, 2, 120, 440, 1, 64), 2, 0),   # n = 26400 over the cap, row/column tables fit: table walker
     ((1, 1, 8, 2200, 1, 64), 2, 1),    # n = 4400 with 1100 local columns: token table
+    ((1, 2, 60, 220, 1, 64), 1, 0),    # k = 1, n = 26400: the member index is the token
 ])
 def test_bf16_row_sources(shp, kf, mode):
-    """The kernel finds a key row's token in one of three ways, chosen by the
-    subsequence sizes; each is checked on sampled rows."""
+    """The kernel finds a key row's token in one of four ways, chosen by k and
+    the subsequence sizes; each is checked on sampled rows."""
     q, k, v = (torch.from_numpy(wl.normal_tensor(shp, 23, i)).to(torch.bfloat16) for i in range(3))
     out = run(q, k, v, kf, mode)
     check_sampled(types.SimpleNamespace(shape=shp), (q, k, v), out, kf, mode, [0], seed=3, tol=TOL["bf16"])
