@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libskiparse.so")
 C_CALLER_SRC = os.path.join(ROOT, "tests", "c_caller.c")
 C_CALLER = os.path.join(HERE, "c_caller")
 
-SOURCES = ["api.hip", "attn_bf16.hip", "block_fp8.hip", "gemm_fp8.hip", "attn_bwd.hip", "attn_f32.hip", "attn_fp8.hip", "index_map.hip", "quant_fp8.hip"]
+SOURCES = ["api.hip", "attn_bf16.hip", "block_fp8.hip", "gemm_fp8.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_f32.hip", "attn_fp8.hip", "index_map.hip", "quant_fp8.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -33,6 +33,11 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+
+# Extra flags per source.  The backward's dQ kernel runs about 7% faster at
+# 720P-5s under LLVM's max-ILP machine scheduler, with the same results; the
+# other kernels are as fast or faster under the default one.
+SOURCE_FLAGS = {"attn_bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc() -> str:
@@ -56,7 +61,7 @@ def build(verbose: bool = False) -> str:
 
     def one(src):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        out = _run([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        out = _run([cc, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
         return obj

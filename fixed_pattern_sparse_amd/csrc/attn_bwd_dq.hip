@@ -1,0 +1,125 @@
+// dQ of the backward pass: queries fixed per work-group, key tiles streamed
+// (the kernel is described with the others in attn_bwd.hip).  Built with the
+// max-ILP machine scheduler, under which it runs about 7% faster at 720P-5s
+// with the same results; the dK/dV kernel is faster under the default one.
+#include "attn_bwd_common.h"
+
+namespace skiparse {
+namespace {
+
+// ---------------------------------------------------------------------------
+// dQ: queries fixed, key tiles streamed
+// ---------------------------------------------------------------------------
+
+template <int ROWS, bool F8>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq_kernel(const AttnArgs a) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  const WorkItem wi = decode_work(a);
+  const SubGeom& sg = wi.sg;
+  const int n = sg.n;
+  const int nkv = (n + kBT - 1) / kBT;
+  const int64_t N = (int64_t)a.g.T * a.g.H * a.g.W;
+  const int64_t base = (int64_t)wi.b * a.batch_stride + (int64_t)wi.head * D;
+  const int64_t rs = a.row_stride;
+  constexpr int EB = F8 ? 1 : 2;   // bytes per element
+  const char* __restrict__ qb = (const char*)a.q + base * EB;
+  const char* __restrict__ dob = (const char*)a.dout + base * EB;
+  const char* __restrict__ kb = (const char*)a.k + base * EB;
+  const char* __restrict__ vb = (const char*)a.v + base * EB;
+
+  Rows<ROWS> rows(a, sg, n);
+  rows.build(tid);
+  const int lrow = tid / kCH, lslot = tid % kCH;
+  const int sw_st = (lslot ^ uswz(lrow)) * 16;
+  auto fetch = [&](int tile, Raw8<F8>& kx, Raw8<F8>& vx) {
+    const int64_t e = (int64_t)rows.tok(tile * kBT + lrow) * rs + lslot * 8;
+    kx = load_raw8<F8>(kb, e);
+    vx = load_raw8<F8>(vb, e);
+  };
+  Raw8<F8> kx, vx;
+  fetch(0, kx, vx);
+
+  // the lane's query: Q and dO fragments (B operands), L and D
+  const int jq = wi.qtile * kBM + wave * 32 + l32;
+  const bool qok = jq < n;
+  const int tq = rows.tok(jq);
+  const int64_t qoff = (int64_t)tq * rs;
+  bf16x8 qf[KK], dof[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qf[kk] = as_bf16x8(load8<F8>(qb, qoff + kk * 16 + hl * 8));
+    dof[kk] = as_bf16x8(load8<F8>(dob, qoff + kk * 16 + hl * 8));
+    __asm__ volatile("" : "+v"(qf[kk]), "+v"(dof[kk]));
+  }
+  const int64_t ridx = ((int64_t)wi.b * N + tq) * a.heads + wi.head;
+  const float lse2 = a.lse[ridx] * kLog2e;
+  const float dq_d = a.dsum[ridx];
+  const float c = F8 ? a.scale_log2 * a.descale[1] * a.descale[3] : a.scale_log2;
+
+  *(uint4*)(gA + lrow * kRowB + sw_st) = widen8<F8>(kx);
+  *(uint4*)(gB + lrow * kRowB + sw_st) = widen8<F8>(vx);
+  __syncthreads();
+
+  floatx16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = floatx16{};
+
+  for (int j = 0; j < nkv; ++j) {
+    const int buf = j & 1;
+    const bool more = j + 1 < nkv;
+    if (more) fetch(j + 1, kx, vx);
+    const char* sK = gA + buf * kTileB;
+    const char* sV = gB + buf * kTileB;
+    floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sK, l32, hl, kk), qf[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sV, l32, hl, kk), dof[kk], dp, 0, 0, 0);
+    }
+    // dS^T = P^T * (dP^T - D); keys past the end of the subsequence get P = 0
+    float ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = j * kBT + (i >> 2) * 8 + hl * 4 + (i & 3);
+      const float p = key < n ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2)) : 0.f;
+      ds[i] = p * (dp[i] - dq_d);
+    }
+    bf16x8 dsb[2];
+    pack_b(ds, dsb);
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols(sK, lane, hl, db, cc), dsb[cc], acc[db], 0, 0, 0);
+    if (more) {
+      *(uint4*)(gA + (buf ^ 1) * kTileB + lrow * kRowB + sw_st) = widen8<F8>(kx);
+      *(uint4*)(gB + (buf ^ 1) * kTileB + lrow * kRowB + sw_st) = widen8<F8>(vx);
+    }
+    __syncthreads();
+  }
+  const float mul = F8 ? a.scale * a.descale_do[1] * a.descale[5] * a.descale[3] : a.scale;
+  if (qok) store_rows_t((__bf16*)a.dq + base + qoff, acc, mul, hl);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq(const AttnArgs& a, bool f8, bool table, hipStream_t stream) {
+  const dim3 grid(a.total_tiles), block(kThreads);
+  if (f8) {
+    if (table) hipLaunchKernelGGL((attn_bwd_dq_kernel<2, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<0, true>), grid, block, 0, stream, a);
+  } else {
+    if (table) hipLaunchKernelGGL((attn_bwd_dq_kernel<2, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<0, false>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace skiparse
