@@ -84,22 +84,9 @@ def subsequence_coord(x, k: int, mode: int):
     return (x // k) % k
 
 
-def local_coord(x, k: int, mode: int):
-    """Position of spatial index ``x`` on its subsequence's local axis.
-
-    token-wise: x // k.  group-wise: (x // k^2) * k + x mod k, i.e. the block
-    row inside the repeating unit of k^2 rows is dropped.
-    """
-    if k == 1:
-        return x
-    if mode == TOKEN:
-        return x // k
-    return (x // (k * k)) * k + x % k
-
-
 def spatial_of_local(xl, p: int, k: int, mode: int):
-    """Inverse of (subsequence_coord, local_coord): the spatial index whose
-    subsequence coordinate is ``p`` and local coordinate is ``xl``."""
+    """The spatial index whose subsequence coordinate is ``p`` and whose
+    position on that subsequence's local axis is ``xl``."""
     if k == 1:
         return xl
     if mode == TOKEN:
@@ -264,14 +251,6 @@ def pad_tokens(x: np.ndarray, k: int) -> np.ndarray:
     out = np.zeros((B, T, Hp, Wp, nh, d), dtype=x.dtype)
     out[:, :, :H, :W] = x
     return out
-
-
-def real_token_mask(T, H, W, k) -> np.ndarray:
-    """(1, T, Hp, Wp, 1, 1) bool: True for real tokens, False for padding."""
-    Hp, Wp = padded_extent(H, k), padded_extent(W, k)
-    m = np.zeros((1, T, Hp, Wp, 1, 1), dtype=bool)
-    m[:, :, :H, :W] = True
-    return m
 
 
 # --- Skiparse-1D: flatten, pad, reshape/transpose --------------------------
