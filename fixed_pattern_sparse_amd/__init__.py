@@ -200,6 +200,9 @@ def _ptr(x):
         return None
     if isinstance(x, int):
         return x
+    if not x.is_contiguous():
+        # every entry point reads and writes dense row-major buffers
+        raise ValueError("tensors passed to libskiparse must be contiguous")
     return x.data_ptr()
 
 
@@ -432,7 +435,8 @@ def attention_train(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, pla
     B, T, H, W, nh, d = q.shape
     if plan is None:
         plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
-    out = torch.empty_like(q)
+    # the kernel writes rows in contiguous order, whatever q's strides are
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, T * H * W, nh), dtype=torch.float32, device=q.device)
     skiparse_attn_fwd_lse(plan, _dtype_code(q), q.contiguous(), k.contiguous(), v.contiguous(), out, lse,
                           softmax_scale)
@@ -443,10 +447,15 @@ def attention_bwd(q, k, v, o, dout, lse, kf: int, mode: int, softmax_scale: floa
                   plan: SkiparsePlan | None = None):
     """Backward pass on bf16 device tensors: returns (dq, dk, dv)."""
     import torch
+    if q.dim() != 6 or any(t.shape != q.shape for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o and dout must share one (B, T, H, W, heads, d) shape")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v, o, dout)):
+        raise TypeError("q, k, v, o and dout must be bfloat16")
     B, T, H, W, nh, d = q.shape
     if plan is None:
         plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    # the kernels write rows in contiguous order, whatever q's strides are
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) for _ in range(3))
     skiparse_attn_bwd(plan, _dtype_code(q), q.contiguous(), k.contiguous(), v.contiguous(), o.contiguous(),
                       dout.contiguous(), lse, dq, dk, dv, softmax_scale)
     return dq, dk, dv

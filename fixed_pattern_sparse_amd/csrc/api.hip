@@ -110,8 +110,10 @@ int fill_attn_args(const skiparse_plan* plan, float softmax_scale, int32_t sub_b
     if (sub_begin != 0) return fail(SKIPARSE_EINVAL, "sub_count == 0 (all) needs sub_begin == 0");
     sub_count = plan->n_sub;
   }
-  if (sub_begin < 0 || sub_count < 0 || sub_begin + sub_count > plan->n_sub)
-    return fail(SKIPARSE_EINVAL, "subsequence range [%d, %d) outside [0, %d)", sub_begin, sub_begin + sub_count, plan->n_sub);
+  // compared without forming sub_begin + sub_count, which can overflow int32
+  if (sub_begin < 0 || sub_count < 0 || sub_begin > plan->n_sub || sub_count > plan->n_sub - sub_begin)
+    return fail(SKIPARSE_EINVAL, "subsequence range [%d, %lld) outside [0, %d)", sub_begin,
+                (long long)sub_begin + sub_count, plan->n_sub);
   if (!(std::isfinite(softmax_scale))) return fail(SKIPARSE_EINVAL, "softmax_scale must be finite");
   const int d = plan->d;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);

@@ -124,6 +124,8 @@ def test_attn_fwd_argument_errors():
     assert _attn_code(p, sb=1, sc=0) == sk.EINVAL
     assert _attn_code(p, sb=3, sc=2) == sk.EINVAL
     assert _attn_code(p, sb=-1, sc=1) == sk.EINVAL
+    assert _attn_code(p, sb=1, sc=2**31 - 1) == sk.EINVAL             # begin + count past int32
+    assert _attn_code(p, sb=2**31 - 1, sc=2**31 - 1) == sk.EINVAL
     assert _attn_code(p, scale=float("inf")) == sk.EINVAL
     assert _attn_code(p, descale=0x5000) == sk.EINVAL                 # descale only for FP8
     assert _attn_code(p, dtype=sk.FP8_E4M3) == sk.EUNSUPPORTED        # FP8 needs d = 128
@@ -153,6 +155,7 @@ def test_attn_fwd_lse_argument_errors():
     assert _fwd_lse_code(p, dtype=sk.F32) == sk.EUNSUPPORTED
     assert _fwd_lse_code(p, dtype=sk.FP8_E4M3) == sk.EUNSUPPORTED
     assert _fwd_lse_code(p, sb=3, sc=2) == sk.EINVAL
+    assert _fwd_lse_code(p, sb=1, sc=2**31 - 1) == sk.EINVAL         # begin + count past int32
     assert _fwd_lse_code(p, scale=float("nan")) == sk.EINVAL
     p96 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 96, 2, 0)
     assert _fwd_lse_code(p96) == sk.EUNSUPPORTED
@@ -186,6 +189,7 @@ def test_attn_bwd_argument_errors():
     assert code(ws=9 * G) == sk.EINVAL                               # workspace overlaps dv
     assert code(dk=6 * G) == sk.EINVAL                               # dk overlaps lse
     assert code(sb=2, sc=3) == sk.EINVAL
+    assert code(sb=1, sc=2**31 - 1) == sk.EINVAL                     # begin + count past int32
     p64 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 64, 2, 0)
     assert code(plan=p64, wb=sk.skiparse_attn_bwd_workspace_bytes(p64)) == sk.EUNSUPPORTED
     bad = sk.skiparse_plan_init(1, 2, 8, 8, 2, 128, 2, 0)
@@ -215,6 +219,7 @@ def test_attn_fwd_lse_fp8_argument_errors():
     assert code(lse=4 * G + 8) == sk.EINVAL                          # lse overlaps the scales
     assert code(lse=5 * G + 1024) == sk.EINVAL                       # lse overlaps o
     assert code(sb=3, sc=2) == sk.EINVAL
+    assert code(sb=1, sc=2**31 - 1) == sk.EINVAL                     # begin + count past int32
     assert code(scale=float("inf")) == sk.EINVAL
     p64 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 64, 2, 0)
     assert code(plan=p64) == sk.EUNSUPPORTED
@@ -247,6 +252,7 @@ def test_attn_bwd_fp8_argument_errors():
     assert code(ws=4 * G) == sk.EINVAL                               # workspace overlaps the Q/K/V scales
     assert code(dv=9 * G + 4096) == sk.EINVAL                        # dv overlaps dq
     assert code(sb=2, sc=3) == sk.EINVAL
+    assert code(sb=1, sc=2**31 - 1) == sk.EINVAL                     # begin + count past int32
     p64 = sk.skiparse_plan_init(1, 2, 8, 8, 2, 64, 2, 0)
     assert code(plan=p64, wb=sk.skiparse_attn_bwd_workspace_bytes(p64)) == sk.EUNSUPPORTED
 

@@ -107,6 +107,28 @@ def test_bwd_deterministic_and_autograd():
         assert torch.equal(x, g)
 
 
+def test_autograd_on_permuted_views():
+    """Q, K, V given as dense permuted views of (B, heads, T, H, W, d) storage
+    (not contiguous in the (B, T, H, W, heads, d) order the library reads):
+    the op's output and all three gradients equal those of the contiguous
+    tensors, in the caller's layout."""
+    shp, kf, mode = (1, 3, 13, 22, 2, 128), 2, 0
+    q, k, v, do = (t.to(DEV) for t in inputs(shp, 405))
+    ref_in = [t.clone().requires_grad_(True) for t in (q, k, v)]
+    o_ref = sk.SkiparseAttention.apply(*ref_in, kf, mode)
+    o_ref.backward(do)
+    # the same values stored head-major, viewed back as (B, T, H, W, heads, d)
+    perm = [t.permute(0, 4, 1, 2, 3, 5).contiguous().permute(0, 2, 3, 4, 1, 5) for t in (q, k, v)]
+    assert not perm[0].is_contiguous() and torch.equal(perm[0], q)
+    views = [t.detach().requires_grad_(True) for t in perm]
+    o_view = sk.SkiparseAttention.apply(*views, kf, mode)
+    o_view.backward(do)
+    torch.cuda.synchronize()
+    assert torch.equal(o_view.detach(), o_ref.detach())
+    for a, b in zip(views, ref_in):
+        assert torch.equal(a.grad, b.grad)
+
+
 def test_bwd_subsequence_ranges():
     """Runs over [0, 1) and [1, 4) give the full call's gradients bit for bit,
     and rows outside the run subsequences are left untouched."""
