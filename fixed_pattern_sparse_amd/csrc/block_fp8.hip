@@ -95,15 +95,15 @@ __global__ void __launch_bounds__(kThreads) rope_amax_kernel(RopeGeom r, const f
                                                              const uint4* __restrict__ x, float* __restrict__ part) {
   __shared__ float2 stage[LDS_TAB ? kTabCap : 1];
   const float2* tab = rope_table<LDS_TAB>(r, gtab, stage);
-  float m = 0.f;
+  uint32_t m = 0;   // bits of max |rope(x)|, NaN-propagating
   for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < r.nvec; i += gridDim.x * kThreads) {
     float v[8];
     rope8(r, tab, x[i], i, v);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(v[j]));
   }
-  m = block_max(m);
-  if (threadIdx.x == 0) part[blockIdx.x] = m;
+  m = block_max_u32(m);
+  if (threadIdx.x == 0) part[blockIdx.x] = __uint_as_float(m);
 }
 
 template <bool LDS_TAB>

@@ -4,7 +4,8 @@
 // HiF8 format is replaced by OCP e4m3 (largest finite value 448).
 //
 // Three streaming passes, all HBM-bound:
-//   1. per-work-group max |x| into the workspace (16-byte loads);
+//   1. per-work-group max |x| into the workspace (16-byte loads); a NaN
+//      anywhere makes the maximum NaN;
 //   2. one work-group reduces the partial maxima and writes {scale, 1/scale},
 //      each an IEEE fp32 division;
 //   3. y = e4m3(x * scale): the fp32 product is clamped to +-448 and
@@ -22,7 +23,7 @@ constexpr int kMaxBlocks = 2048;
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const void* __restrict__ x, int64_t numel,
                                                                  float* __restrict__ part) {
-  float m = 0.f;
+  uint32_t m = 0;                    // bits of max |x|, NaN-propagating
   constexpr int VE = BF16 ? 8 : 4;   // elements per 16-byte vector
   const int64_t nvec = numel / VE;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -32,30 +33,31 @@ __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const void* __re
     if (BF16) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[e] & 0xFFFFu)));
-        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[e] >> 16)));
+        m = max(m, abs_bits(bf16_bits_to_f32(w[e] & 0xFFFFu)));
+        m = max(m, abs_bits(bf16_bits_to_f32(w[e] >> 16)));
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(__uint_as_float(w[e])));
+      for (int e = 0; e < 4; ++e) m = max(m, abs_bits(__uint_as_float(w[e])));
     }
   }
   if (blockIdx.x == 0) {   // scalar tail
     for (int64_t i = nvec * VE + threadIdx.x; i < numel; i += kThreads) {
       const float v = BF16 ? bf16_bits_to_f32(((const uint16_t*)x)[i]) : ((const float*)x)[i];
-      m = fmaxf(m, fabsf(v));
+      m = max(m, abs_bits(v));
     }
   }
-  m = block_max(m);
-  if (threadIdx.x == 0) part[blockIdx.x] = m;
+  m = block_max_u32(m);
+  if (threadIdx.x == 0) part[blockIdx.x] = __uint_as_float(m);
 }
 
 __global__ void __launch_bounds__(kThreads) scale_kernel(const float* __restrict__ part, int nparts, float fp8_max,
                                                          float eps, float* __restrict__ scale) {
-  float m = 0.f;
-  for (int i = threadIdx.x; i < nparts; i += kThreads) m = fmaxf(m, part[i]);
-  m = block_max(m);
+  uint32_t mb = 0;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) mb = max(mb, abs_bits(part[i]));
+  const float m = __uint_as_float(block_max_u32(mb));
   if (threadIdx.x == 0) {
+    // a NaN maximum gives a NaN scale, so every code of the tensor is NaN
     const float s = fp8_max / (m + eps);
     scale[0] = s;
     scale[1] = 1.0f / s;

@@ -273,8 +273,10 @@ size_t skiparse_quant_fp8_workspace_bytes(int64_t numel);
  *   dev_scale  device, 2 fp32: {scale, 1/scale}
  *   workspace  device, >= skiparse_quant_fp8_workspace_bytes(numel) bytes,
  *              contents need not be initialized; it is overwritten
- * Inputs must be finite.  Errors: SKIPARSE_EINVAL, SKIPARSE_EWORKSPACE,
- * SKIPARSE_EHIP.
+ * Non-finite inputs are not hidden: a NaN anywhere makes amax, the scale and
+ * every code NaN (code 0xFF); an infinity makes the scale 0, so finite
+ * elements become signed zeros and the infinities NaN.  Errors:
+ * SKIPARSE_EINVAL, SKIPARSE_EWORKSPACE, SKIPARSE_EHIP.
  */
 int skiparse_quant_fp8(const void* x, skiparse_dtype x_dtype, int64_t numel, uint8_t* y,
                        float* dev_scale, float fp8_max, float eps,

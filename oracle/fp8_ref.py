@@ -14,7 +14,16 @@ OCP E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits.
   exponent 15, m = 7    -> NaN (no infinities); largest finite value 448.
 
 Encoding used here: round to nearest, ties to even, saturating to +-448 for
-magnitudes at or above 464 (the midpoint past 448); the sign of zero is kept.
+magnitudes at or above 464 (the midpoint past 448, infinities included); the
+sign of zero is kept.  NaN has two codes in the format (either sign); this
+build writes every NaN as 0xFF (S.1111.111 with the sign bit set), the code
+gfx950's fp32 -> e4m3 conversion instruction produces for a NaN.
+
+Non-finite tensors: Amax is the largest magnitude, so a NaN anywhere makes
+Amax and the scale NaN and every product NaN (all codes 0xFF); an infinity
+makes the scale 0, finite elements become signed zeros and the infinities
+themselves (inf * 0) NaN.  A diverging tensor therefore shows up in its codes
+instead of being hidden behind finite values.
 """
 
 from __future__ import annotations
@@ -44,12 +53,16 @@ _TABLE = e4m3_decode_table()
 _POS = _TABLE[:127]  # codes 0x00..0x7E, non-negative finite, increasing
 
 
+NAN_CODE = 0xFF
+
+
 def e4m3_encode(x) -> np.ndarray:
-    """Encode finite values (float64/float32 array) to E4M3 codes (uint8)."""
-    a = np.abs(np.asarray(x, np.float64))
-    neg = np.signbit(np.asarray(x, np.float64))
-    if not np.all(np.isfinite(a)):
-        raise ValueError("e4m3_encode expects finite input")
+    """Encode values (float64/float32 array) to E4M3 codes (uint8); NaN gives
+    0xFF, infinities saturate."""
+    xd = np.asarray(x, np.float64)
+    nan = np.isnan(xd)
+    a = np.abs(np.where(nan, 0.0, xd))
+    neg = np.signbit(xd)
     hi = np.searchsorted(_POS, a, side="left")          # first value >= a
     hi = np.clip(hi, 0, 126)
     lo = np.clip(hi - 1, 0, 126)
@@ -58,7 +71,8 @@ def e4m3_encode(x) -> np.ndarray:
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
     code = np.where(a >= _POS[hi], hi, np.where(pick_hi, hi, lo))
     code = np.where(a >= 464.0, 126, code)              # saturate
-    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+    code = code | np.where(neg, 0x80, 0)
+    return np.where(nan, NAN_CODE, code).astype(np.uint8)
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -79,9 +93,11 @@ def quantize_per_tensor(x, fp8_max=E4M3_MAX, eps=1e-12):
     is encoded with :func:`e4m3_encode`.
     """
     xf = np.asarray(x, np.float32)
+    # np.max propagates NaN: one NaN element makes Amax NaN
     amax = np.float32(np.max(np.abs(xf))) if xf.size else np.float32(0.0)
-    scale = per_tensor_scale(amax, fp8_max, eps)
-    prod = (xf * scale).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        scale = per_tensor_scale(amax, fp8_max, eps)
+        prod = (xf * scale).astype(np.float32)
     return e4m3_encode(prod), scale, amax
 
 

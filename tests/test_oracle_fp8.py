@@ -92,3 +92,57 @@ def test_per_tensor_quantization(seed):
 def test_zero_tensor_scale_is_finite():
     codes, scale, amax = f8.quantize_per_tensor(np.zeros(16, np.float32))
     assert amax == 0 and np.isfinite(scale) and np.all(codes == 0)
+
+
+def test_nan_and_infinity_codes():
+    """NaN has the codes S.1111.111 in the format; the encoder writes 0xFF for
+    every NaN (torch agrees the code decodes to NaN), and infinities saturate
+    like every other magnitude at or past 464."""
+    codes = f8.e4m3_encode(np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0]))
+    np.testing.assert_array_equal(codes, np.array([0xFF, 0xFF, 0x7E, 0xFE, 0x00, 0x80], np.uint8))
+    tv = torch.tensor([0xFF], dtype=torch.uint8).view(torch.float8_e4m3fn).float()
+    assert torch.isnan(tv).all()
+    assert torch_encode(np.array([np.nan]))[0] & 0x7F == 0x7F   # torch's NaN is a NaN code too
+
+
+def _planted_fmax_quantize(x, fp8_max=448.0, eps=1e-12):
+    """A plausible mistake: Amax taken with a NaN-dropping max (like fmaxf)."""
+    xf = np.asarray(x, np.float32)
+    amax = np.float32(np.nanmax(np.abs(xf)))
+    scale = f8.per_tensor_scale(amax, fp8_max, eps)
+    return f8.e4m3_encode((np.nan_to_num(xf) * scale).astype(np.float32)), scale, amax
+
+
+def test_per_tensor_nan_poisons_the_tensor():
+    """One NaN makes Amax, the scale and every code NaN, so a diverging step
+    cannot hide behind finite codes; the NaN-dropping max fails this."""
+    x = np.linspace(-3, 3, 101).astype(np.float32)
+    x[17] = np.nan
+    codes, scale, amax = f8.quantize_per_tensor(x)
+    assert np.isnan(amax) and np.isnan(scale)
+    assert np.all(codes == 0xFF)
+    pc, ps, pa = _planted_fmax_quantize(x)
+    assert not np.all(pc == 0xFF) and np.isfinite(ps)
+
+
+def test_per_tensor_infinity():
+    """An infinity makes Amax inf and the scale 0: finite elements go to signed
+    zero, the infinities (inf * 0) to NaN."""
+    x = np.array([1.5, -2.0, np.inf, 0.25, -np.inf], np.float32)
+    codes, scale, amax = f8.quantize_per_tensor(x)
+    assert np.isinf(amax) and scale == 0.0
+    np.testing.assert_array_equal(codes, np.array([0x00, 0x80, 0xFF, 0x00, 0xFF], np.uint8))
+
+
+def test_unit_scale_with_eps_zero():
+    """fp8_max equal to the tensor's Amax and eps = 0 give the scale 1.0 exactly,
+    so the codes are the plain encoding of the values (the setting the device
+    edge-case test uses)."""
+    vals = np.array([448.0, -3.1, 2.0 ** -9, 2.0 ** -10, 0.0], np.float32)
+    codes, scale, amax = f8.quantize_per_tensor(vals, fp8_max=448.0, eps=0.0)
+    assert scale == 1.0 and amax == 448.0
+    np.testing.assert_array_equal(codes, f8.e4m3_encode(vals))
+    big = np.array([1000.0, 455.0, 464.0, -470.0], np.float32)
+    codes, scale, amax = f8.quantize_per_tensor(big, fp8_max=1000.0, eps=0.0)
+    assert scale == 1.0
+    np.testing.assert_array_equal(codes, np.array([0x7E, 0x7E, 0x7E, 0xFE], np.uint8))
