@@ -84,6 +84,7 @@ EXPORTED = (
     "skiparse_attn_fwd_lse_fp8",
     "skiparse_attn_bwd_fp8",
     "skiparse_quant_fp8_workspace_bytes",
+    "skiparse_quant_fp8_noalloc",
     "skiparse_quant_fp8",
     "skiparse_block_workspace_bytes",
     "skiparse_block_fwd_fp8",
@@ -171,6 +172,9 @@ def lib():
     L.skiparse_quant_fp8.restype = ctypes.c_int
     L.skiparse_quant_fp8.argtypes = [vp, ctypes.c_int, ctypes.c_int64, vp, vp, ctypes.c_float, ctypes.c_float,
                                      vp, ctypes.c_size_t, vp]
+    L.skiparse_quant_fp8_noalloc.restype = ctypes.c_int
+    L.skiparse_quant_fp8_noalloc.argtypes = [vp, ctypes.c_int, ctypes.c_int64, vp, vp, ctypes.c_float, ctypes.c_float,
+                                             vp]
     L.skiparse_block_workspace_bytes.restype = ctypes.c_size_t
     L.skiparse_block_workspace_bytes.argtypes = [P]
     L.skiparse_block_fwd_fp8.restype = ctypes.c_int
@@ -319,6 +323,17 @@ def skiparse_quant_fp8(x, y, scale, fp8_max: float = 448.0, eps: float = 1e-12, 
     wb = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     _check(lib().skiparse_quant_fp8(_ptr(x), x_dtype, numel, _ptr(y), _ptr(scale), float(fp8_max), float(eps),
                                     _ptr(workspace), wb, _stream(stream)))
+    return y
+
+
+def skiparse_quant_fp8_noalloc(x, y, scale, fp8_max: float = 448.0, eps: float = 1e-12, stream=None, x_dtype=None):
+    """skiparse_quant_fp8 with the library's own scratch: allocates nothing.
+    Calls that overlap in time on one GPU race (one shared scratch per GPU)."""
+    import torch
+    if x_dtype is None:
+        x_dtype = BF16 if x.dtype == torch.bfloat16 else F32
+    _check(lib().skiparse_quant_fp8_noalloc(_ptr(x), x_dtype, x.numel(), _ptr(y), _ptr(scale), float(fp8_max),
+                                            float(eps), _stream(stream)))
     return y
 
 

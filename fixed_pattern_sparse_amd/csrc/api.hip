@@ -483,6 +483,32 @@ int skiparse_quant_fp8(const void* x, skiparse_dtype x_dtype, int64_t numel, uin
   return ok();
 }
 
+int skiparse_quant_fp8_noalloc(const void* x, skiparse_dtype x_dtype, int64_t numel, uint8_t* y, float* dev_scale,
+                               float fp8_max, float eps, hipStream_t stream) {
+  if (x_dtype != SKIPARSE_BF16 && x_dtype != SKIPARSE_F32)
+    return fail(SKIPARSE_EINVAL, "x_dtype must be BF16 or F32");
+  if (numel < 1) return fail(SKIPARSE_EINVAL, "numel must be >= 1");
+  if (!x || !y || !dev_scale) return fail(SKIPARSE_EINVAL, "x, y and dev_scale must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)dev_scale & 3u) != 0)
+    return fail(SKIPARSE_EINVAL, "x and y must be 16-byte aligned, dev_scale 4-byte aligned");
+  if (!(fp8_max > 0.f) || !std::isfinite(fp8_max) || !(eps >= 0.f) || !std::isfinite(eps))
+    return fail(SKIPARSE_EINVAL, "fp8_max must be positive and eps non-negative, both finite");
+  const size_t need = quant_workspace_bytes(numel);
+  if (need > quant_scratch_bytes())
+    return fail(SKIPARSE_EWORKSPACE, "numel=%lld needs %zu bytes of scratch, above the %zu the library holds",
+                (long long)numel, need, quant_scratch_bytes());
+  const size_t xb = (size_t)numel * (x_dtype == SKIPARSE_BF16 ? 2 : 4);
+  if (overlap(y, (size_t)numel, x, xb) || overlap(dev_scale, 8, x, xb) || overlap(dev_scale, 8, y, (size_t)numel))
+    return fail(SKIPARSE_EINVAL, "x, y and dev_scale must not overlap");
+  float* ws = nullptr;
+  hipError_t e = quant_scratch(&ws);
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "scratch lookup failed: %s", hipGetErrorString(e));
+  (void)hipGetLastError();
+  e = launch_quant_fp8(x, x_dtype == SKIPARSE_BF16, numel, y, dev_scale, fp8_max, eps, ws, stream);
+  if (e != hipSuccess) return fail(SKIPARSE_EHIP, "quantization launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 // ---------------------------------------------------------------------------
 // fp8 attention block
 // ---------------------------------------------------------------------------

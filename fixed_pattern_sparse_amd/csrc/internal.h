@@ -57,6 +57,10 @@ hipError_t launch_attn_bwd_fp8(AttnArgs a, int B, int d, hipStream_t stream);
 hipError_t launch_index_map(const Geom& g, const SubGeom* subs, int n_sub, int sub_h, int sub_w,
                             int32_t* out, hipStream_t stream);
 size_t quant_workspace_bytes(int64_t numel);
+// The allocation-free quantizer's scratch: its capacity in bytes, and this
+// GPU's device address of it (looked up once per device).
+size_t quant_scratch_bytes();
+hipError_t quant_scratch(float** out);
 hipError_t launch_quant_fp8(const void* x, int x_is_bf16, int64_t numel, uint8_t* y, float* scale,
                             float fp8_max, float eps, void* ws, hipStream_t stream);
 

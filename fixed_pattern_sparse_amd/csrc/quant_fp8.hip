@@ -11,6 +11,9 @@
 //   3. y = e4m3(x * scale): the fp32 product is clamped to +-448 and
 //      converted by v_cvt_pk_fp8_f32 (round to nearest even), which equals
 //      round-to-nearest-even with saturation.
+#include <atomic>
+#include <mutex>
+
 #include "fp8_codec.h"
 #include "block.h"
 
@@ -106,9 +109,45 @@ int blocks_for(int64_t numel) {
   return (int)b;
 }
 
+// Scratch of the allocation-free entry point: room for the partial maxima of
+// the largest grid (kMaxBlocks work-groups, 8 KiB), so it serves every numel.
+// One copy per GPU, held until the process ends; every call on a GPU shares it.
+static __device__ __align__(256) float scratch[kMaxBlocks];
+
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
 }  // namespace
 
 size_t quant_workspace_bytes(int64_t numel) { return (size_t)blocks_for(numel) * sizeof(float); }
+
+size_t quant_scratch_bytes() { return sizeof(scratch); }
+
+// Device address of this GPU's copy of the scratch array, looked up once per
+// device with that device current.  In host code the array's name is only a
+// host-side stand-in, never a device address.
+hipError_t quant_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* a = nullptr;
+      e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (a == nullptr) return hipErrorInvalidSymbol;
+      p = (float*)a;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 hipError_t launch_fp8_scale(const float* part, int nparts, float fp8_max, float eps, float* scale,
                             hipStream_t stream) {

@@ -283,6 +283,23 @@ int skiparse_quant_fp8(const void* x, skiparse_dtype x_dtype, int64_t numel, uin
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * skiparse_quant_fp8 for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same quantization, with the per-work-group partial maxima
+ * in a scratch array the library holds on each GPU (8 KiB, room for the
+ * largest grid, so every numel >= 1 fits; a size past it would be refused
+ * with SKIPARSE_EWORKSPACE).  The array lives until the process ends; its
+ * device address is looked up once per GPU, on the first call with that GPU
+ * current.  Nothing is allocated, freed or synchronized.  Every call on one
+ * GPU shares the array: calls that overlap in time on one GPU (different
+ * streams, or threads) race and must be serialized by the caller.  Each call
+ * writes every partial it reads, so nothing needs clearing between calls.
+ * Arguments, results and errors as skiparse_quant_fp8.
+ */
+int skiparse_quant_fp8_noalloc(const void* x, skiparse_dtype x_dtype, int64_t numel, uint8_t* y,
+                               float* dev_scale, float fp8_max, float eps, hipStream_t stream);
+
+/*
  * One attention block of the 8-bit video DiT around the sparse attention.
  * The DiT trains and runs with per-tensor 8-bit quantization,
  * scale = fp8_max / (amax + eps) (OSP-Next summary, 方法步骤详情 method steps;
