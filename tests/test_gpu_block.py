@@ -296,10 +296,6 @@ def test_block_720p_tokens_12_heads_sampled():
     assert torch.equal(y2.float(), 2.0 * y1.float())
 
 
-@pytest.mark.skip(reason="the block's first version, with its projections on hipBLASLt, faulted the GPU at this "
-                         "shape; no mistake in the block's own kernels was found by reading them (their indexing "
-                         "is checked on the CPU at this shape), the projections now run on the library's own GEMM, "
-                         "tested on its own at this shape, and this case stays off the GPU until a cause is shown")
 def test_block_workload_sampled():
     """720P-5s (21 x 45 x 80 tokens, 40 heads of 128, k = 2 token-wise): rows
     against the exact block, and exact doubling with Wo's scale halved."""
