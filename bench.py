@@ -10,8 +10,9 @@ same subsequence) pairs, ms per step, the roofline of the attention kernel
 (average launch duration from HIP events on the launch stream), the oracle's
 CPU baseline on a bounded sample, and extras: ms per layer, the same kernel at
 k = 1 (full attention), the fp8 path, a training step (forward with the
-log-sum-exp, backward), Skiparse-1D, and the fp8 block's projection GEMM and
-rotary quantizer.
+log-sum-exp, backward), Skiparse-1D, the fp8 block's projection GEMM, rotary
+quantizer and whole block, and the other bf16 workloads (768P-5s unpadded,
+480P with its k = 1 layer).
 """
 
 from __future__ import annotations
@@ -84,11 +85,78 @@ def cpu_baseline(workload, cpu_inputs, budget_s=20.0):
         "value": round(tflops, 6),
         "unit": "TFLOP/s",
         "cores": cb.blas_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{units} (batch, head, subsequence) units = heads 0-{heads_done - 1} of batch 0, all "
                    f"{workload.k * workload.k} subsequences of both patterns; {pairs:.4g} pairs in "
                    f"{secs:.1f} s, fp32 numpy/BLAS; TFLOP/s scales exactly by pair count"),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_layers(sk, stream, plans, q, k, v, out, reps):
+    """ms of one pass over ``plans`` (bf16 forward layers back to back),
+    averaged over ``reps`` passes after one untimed pass."""
+    import torch
+    for pl in plans:
+        sk.skiparse_attn_fwd(pl, sk.BF16, q, k, v, out, stream=stream)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    for _ in range(reps):
+        for pl in plans:
+            sk.skiparse_attn_fwd(pl, sk.BF16, q, k, v, out, stream=stream)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    return e[0].elapsed_time(e[1]) / reps
+
+
+def other_workloads(sk, stream, ref_rate):
+    """The other bf16 forward configurations, each timed on its own inputs:
+    768P-5s (B = 2, no padding) token-wise and group-wise layers separately
+    and back to back, and 480P with both patterns and its k = 1 layer.  Inputs
+    are N(0,1) from torch's device generator with a fixed seed, rounded to
+    bf16.  ``ref_rate`` is the padded 720P-5s layer rate of the same run, for
+    the padded / unpadded per-pair comparison."""
+    import torch
+    import workloads as wl
+    res = {}
+    for name, reps in (("768p_5s", 3), ("480p", 10)):
+        w = wl.WORKLOADS[name]
+        B, T, H, W, nh, d = w.shape
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed)
+        q, k, v = (torch.randn(w.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(3))
+        out = torch.empty_like(q)
+        p_tok = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, sk.MODE_TOKEN)
+        p_grp = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, sk.MODE_GROUP)
+        r = {"shape": list(w.shape), "k": w.k, "padded": [p_tok.Hp, p_tok.Wp] != [H, W]}
+        for tag, plans in (("token", [p_tok]), ("group", [p_grp]), ("token_then_group", [p_tok, p_grp])):
+            ms = time_layers(sk, stream, plans, q, k, v, out, reps)
+            fl = sum(pl.flops for pl in plans)
+            r[tag] = {"ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                      "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+        if name == "480p":
+            p1 = sk.skiparse_plan_init(B, T, H, W, nh, d, 1, sk.MODE_TOKEN)
+            ms = time_layers(sk, stream, [p1], q, k, v, out, reps)
+            r["k1_full"] = {"ms": round(ms, 3), "tflops": round(p1.flops / (ms * 1e-3) / 1e12, 2)}
+            r["speedup_vs_k1"] = round(ms / r["token"]["ms"], 3)
+        else:
+            r["per_pair_rate_vs_720p_padded"] = round(r["token_then_group"]["tflops"] / ref_rate, 4)
+        res[name] = r
+        del q, k, v, out
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -424,8 +492,40 @@ def main():
                                                    "attention_tflop": round(pl.flops / 1e12, 3),
                                                    "projection_tflop": round(4 * 2 * M7 * C4 * C4 / 1e12, 3)}
         del x7, y7, bf
+        # the block at its real shape: 720P-5s with all 40 heads (C = 5120);
+        # x and the weights are N(0,1) from torch's device generator with a
+        # fixed seed (weights scaled by 1/sqrt(C)), rounded to bf16 / e4m3
+        Cf = nh * d
+        gb = torch.Generator(device="cuda")
+        gb.manual_seed(w.seed + 7)
+        xf = torch.randn((B, T, H, W, Cf), generator=gb, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        wf = [torch.randn((Cf, Cf), generator=gb, device="cuda", dtype=torch.float32) * (1.0 / np.sqrt(Cf))
+              for _ in range(4)]
+        wf_codes, wf_scales = sk.quantize_weights(*wf)
+        del wf
+        for mode, name in ((sk.MODE_TOKEN, "token"), (sk.MODE_GROUP, "group")):
+            pl = sk.skiparse_plan_init(B, T, H, W, nh, d, w.k, mode)
+            bf = sk.BlockFP8(wf_codes, wf_scales, nh, w.k, mode)
+            yf = bf(xf)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            for _ in range(3):
+                bf(xf, out=yf)
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            ms = e[0].elapsed_time(e[1]) / 3
+            flops = pl.flops + 4 * 2 * M * Cf * Cf
+            block[f"block_720p_5s_40_heads_{name}"] = {
+                "ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                "attention_tflop": round(pl.flops / 1e12, 3), "projection_tflop": round(4 * 2 * M * Cf * Cf / 1e12, 3)}
+            del yf, bf
+        del xf, wf_codes, wf_scales
+        torch.cuda.empty_cache()
         extras["block_fp8"] = block
         del w_codes, w_scales
+        del k, v, o_tok, o_grp
+        torch.cuda.empty_cache()
+        extras["bf16_other_workloads"] = other_workloads(sk, stream, tflops)
     result["extras"] = extras
 
     if not args.no_cpu_baseline:
