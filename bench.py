@@ -268,6 +268,11 @@ def main():
     extras = {"ms_per_layer": round(ms_step / 2, 4)}
 
     if not args.no_extras:
+        t_x = time.time()
+
+        def progress(name):
+            print(f"# extras: {name} done at {time.time() - t_x:.1f} s", file=sys.stderr, flush=True)
+
         # same kernel at k = 1 (full attention, the hybrid model's full layers)
         p1 = sk.skiparse_plan_init(B, T, H, W, nh, d, 1, sk.MODE_TOKEN)
         o1 = torch.empty_like(q)
@@ -282,6 +287,7 @@ def main():
         extras["k1_ms_per_layer"] = round(k1_ms, 3)
         extras["k1_tflops"] = round(p1.flops / (k1_ms * 1e-3) / 1e12, 3)
         extras["speedup_vs_k1"] = round(k1_ms / avg_launch_ms, 3)
+        progress("k = 1 layer")
         del o1
         # fp8 path on the same shape: per-tensor e4m3 quantization of Q, K, V
         # (scale = 448 / (amax + 1e-12)) then the e4m3 kernel, k = 2 and k = 4
@@ -316,6 +322,7 @@ def main():
         fp8["quantize_qkv"] = {"ms": round(qms, 3), "GBps": round(qbytes / (qms * 1e-3) / 1e9, 1),
                                "frac_hbm_peak": round(qbytes / (qms * 1e-3) / 1e9 / HBM_GBS, 4)}
         extras["fp8_e4m3"] = fp8
+        progress("e4m3 forward")
         del o8, codes
         # training step of one layer: forward keeping the log-sum-exp, then the
         # backward pass for a synthetic upstream gradient.  Backward FLOPs are
@@ -346,6 +353,7 @@ def main():
                            "bwd_frac_bf16_peak": round(2.5 * pl.flops / (bms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
             del ot, lse, grads, ws
         extras["training_bf16"] = train
+        progress("bf16 training step")
         # the 8-bit training step (token-wise): Q, K, V and dO quantized per
         # tensor on the device, the e4m3 forward keeping the log-sum-exp, then
         # the backward on the codes; quantization of dO is timed with the
@@ -388,6 +396,7 @@ def main():
             "note": "e4m3 tensors, quantization included; the backward's products run on bf16 MFMA"}
         del sc8, dsc8, c8, qws, ot, lse, grads, ws
         del do_
+        progress("8-bit training step")
         # Skiparse-1D on the same shape (the 1D rule on each frame's flattened
         # (h, w), stride k*k: the variant the 2D pattern is compared with)
         one_d = {}
@@ -404,6 +413,7 @@ def main():
             ms = e[0].elapsed_time(e[1]) / 3
             one_d[name] = {"ms": round(ms, 3), "tflops": round(pl.flops / (ms * 1e-3) / 1e12, 2), "pairs": int(pl.pairs)}
         extras["skiparse_1d_bf16"] = one_d
+        progress("Skiparse-1D")
         del o1d
         # pieces of the fp8 attention block at C = heads * d channels: the
         # e4m3 projection GEMM (2 * tokens * C * C FLOPs) and the rotary
@@ -522,10 +532,12 @@ def main():
         del xf, wf_codes, wf_scales
         torch.cuda.empty_cache()
         extras["block_fp8"] = block
+        progress("fp8 block")
         del w_codes, w_scales
         del k, v, o_tok, o_grp
         torch.cuda.empty_cache()
         extras["bf16_other_workloads"] = other_workloads(sk, stream, tflops)
+        progress("768P-5s and 480P layers")
     result["extras"] = extras
 
     if not args.no_cpu_baseline:

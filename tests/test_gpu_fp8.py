@@ -95,4 +95,5 @@ def test_fp8_workload_sampled(kf, mode):
         toks = np.unique(np.array(toks, np.int64))
         r = ref.attention_rows(lq, lk, lv, T, H, W, kf, mode, 0, h, toks)
         worst = max(worst, err_ratio(on[0, toks, h], r))
+    print(f"\n[sampled parity] 720p_5s_fp8 k={kf} mode={mode} e4m3: max err {worst:.3e} of max(1, max|O|)")
     assert worst <= TOL, worst

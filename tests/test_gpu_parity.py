@@ -229,7 +229,8 @@ def test_bf16_workload_sampled(name, kf, mode):
     out = sk.attention(*dev, kf, mode)
     torch.cuda.synchronize()
     heads = [0, w.heads // 2, w.heads - 1]
-    check_sampled(w, cpu, out, kf, mode, heads, seed=kf * 10 + mode, tol=TOL["bf16"])
+    worst = check_sampled(w, cpu, out, kf, mode, heads, seed=kf * 10 + mode, tol=TOL["bf16"])
+    print(f"\n[sampled parity] {name} k={kf} mode={mode} bf16: max err {worst:.3e} of max(1, max|O|)")
 
 
 @pytest.mark.parametrize("shp,kf,mode", [
