@@ -393,7 +393,7 @@ def main():
         extras["training_fp8_token"] = {
             "fwd_lse_ms": round(fms, 3), "bwd_ms": round(bms, 3),
             "bwd_tflops": round(2.5 * pl.flops / (bms * 1e-3) / 1e12, 2),
-            "note": "e4m3 tensors, quantization included; the backward's products run on bf16 MFMA"}
+            "note": "e4m3 tensors, quantization included; S and dP on the e4m3 matrix core, dV, dK, dQ on bf16 MFMA"}
         del sc8, dsc8, c8, qws, ot, lse, grads, ws
         del do_
         progress("8-bit training step")

@@ -25,10 +25,12 @@
 //                        dK^T += Q^T (P * dP).
 // 8-bit inputs (F8): Q, K, V and dO arrive as per-tensor e4m3 codes with
 // their scales (the pages quantize every tensor of the 8-bit training path
-// per tensor, the gradient with its own maximum).  The loaders widen each code
-// to bf16, which is exact (every e4m3 value is a bf16 value), so the MFMA
-// products of codes are exact as on the 8-bit matrix core; the descales fold
-// into scalars: the exp2 constant takes 1/(s_q s_k), D enters as D / f with
+// per tensor, the gradient with its own maximum).  S and dP, the products of
+// two coded tensors, run on the e4m3 matrix core (v_mfma_*_32x32x64_f8f6f4)
+// from e4m3 copies of the staged tiles and code fragments in registers; the
+// transposed operands of dV, dK and dQ come from bf16 copies, widened from the
+// codes at staging (exact: every e4m3 value is a bf16 value), against P and dS
+// in bf16.  The descales fold into scalars: the exp2 constant takes 1/(s_q s_k), D enters as D / f with
 // f = 1/(s_do s_v) so dP - D is f (dO^ V^T - D/f), and the outputs take
 // scale f / s_k (dQ), scale f / s_q (dK) and 1/s_do (dV).
 // Per-query L and D enter the dK/dV kernel through the MFMA accumulator's
@@ -119,6 +121,10 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
   auto stash = [&](int buf, const Raw8<F8>& qx, const Raw8<F8>& dx, float ln, float dn) {
     *(uint4*)(gA + buf * kTileB + lrow * kRowB + sw_st) = widen8<F8>(qx);
     *(uint4*)(gB + buf * kTileB + lrow * kRowB + sw_st) = widen8<F8>(dx);
+    if constexpr (F8) {   // codes for the e4m3 products S and dP
+      stash8(gA8 + buf * kTileB8, lrow, lslot, qx);
+      stash8(gB8 + buf * kTileB8, lrow, lslot, dx);
+    }
     if (lslot == 0) {
       gL[buf * kBT + lrow] = ln;
       gDn[buf * kBT + lrow] = dn;
@@ -135,19 +141,30 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
   for (int i = 0; i < kBM * kCH / kThreads; ++i) {
     const int r = lrow + i * kBT;
     const int64_t e = (int64_t)rows.tok(key0 + r) * rs + lslot * 8;
-    *(uint4*)(gVk + r * kRowB + (lslot ^ uswz(r)) * 16) = load8<F8>(vb, e);
+    if constexpr (F8) stash8(gVk8, r, lslot, load_raw8<true>(vb, e));   // as codes
+    else *(uint4*)(gVk + r * kRowB + (lslot ^ uswz(r)) * 16) = load8<F8>(vb, e);
   }
 
   const int jk = key0 + wave * 32 + l32;
   const bool kok = jk < n;
   const int64_t koff = (int64_t)rows.tok(jk) * rs;
-  bf16x8 kf[KK];
+  bf16x8 kf[KK];   // bf16 path
+  intx8 kf8[2];    // 8-bit path: codes for the e4m3 matrix core
+  if constexpr (F8) {
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    kf[kk] = as_bf16x8(load8<F8>(kb, koff + kk * 16 + hl * 8));
-    __asm__ volatile("" : "+v"(kf[kk]));
+    for (int kk = 0; kk < 2; ++kk) {
+      kf8[kk] = frag8_global(kb + koff, hl, kk);
+      __asm__ volatile("" : "+v"(kf8[kk]));
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      kf[kk] = as_bf16x8(load8<F8>(kb, koff + kk * 16 + hl * 8));
+      __asm__ volatile("" : "+v"(kf[kk]));
+    }
   }
-  const char* sVk = gVk + wave * 32 * kRowB;   // the wave's 32 key rows
+  const char* sVk = gVk + wave * 32 * kRowB;     // the wave's 32 key rows
+  const char* sVk8 = gVk8 + wave * 32 * kRowB8;  // the same as codes (8-bit path)
 
   stash(0, qx, dx, ln, dn);
   __syncthreads();
@@ -173,9 +190,16 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[g * 4 + e] = l4[e];
     }
+    if constexpr (F8) {
+      const char* sQ8 = gA8 + buf * kTileB8;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sQ, l32, hl, kk), kf[kk], s, 0, 0, 0);
+      for (int kk = 0; kk < 2; ++kk)
+        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag8_rows(sQ8, l32, hl, kk), kf8[kk], s, 0, 0, 0, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sQ, l32, hl, kk), kf[kk], s, 0, 0, 0);
+    }
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] * c);
@@ -195,9 +219,17 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dp[g * 4 + e] = d4[e];
     }
+    if constexpr (F8) {
+      const char* sD8 = gB8 + buf * kTileB8;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sD, l32, hl, kk), frag_rows(sVk, l32, hl, kk), dp, 0, 0, 0);
+      for (int kk = 0; kk < 2; ++kk)
+        dp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag8_rows(sD8, l32, hl, kk), frag8_rows(sVk8, l32, hl, kk),
+                                                             dp, 0, 0, 0, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sD, l32, hl, kk), frag_rows(sVk, l32, hl, kk), dp, 0, 0, 0);
+    }
     // dS = P * (dP - D), with P taken back from its bf16 copy (the value the
     // dV product used), so the fp32 P need not stay live
     float ds[16];

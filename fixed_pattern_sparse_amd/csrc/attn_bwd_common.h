@@ -17,6 +17,7 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef int intx8 __attribute__((ext_vector_type(8)));
 
 constexpr int D = 128;              // head dim (the only one built for the backward pass)
 constexpr int KK = D / 16;          // MFMA steps over d
@@ -29,6 +30,8 @@ constexpr int kRowB = D * 2;        // bytes per row
 constexpr int kTileB = kBT * kRowB; // 8 KB
 constexpr int kCH = D / 8;          // 16-byte chunks per row
 constexpr int kTokCap = 24064;
+constexpr int kRowB8 = D;          // bytes per row of e4m3 codes
+constexpr int kTileB8 = kBT * kRowB8;  // 4 KB
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(kBT * kCH == kThreads, "one chunk per thread and matrix per tile");
 
@@ -38,10 +41,43 @@ __shared__ __attribute__((aligned(16))) char gVk[kBM * kRowB];  // dK/dV kernel:
 __shared__ __attribute__((aligned(16))) float gL[2 * kBT];     // dK/dV kernel: -L/c per query row
 __shared__ __attribute__((aligned(16))) float gDn[2 * kBT];    // dK/dV kernel: -D per query row
 __shared__ int32_t gTokB[kTokCap];
+// 8-bit path: e4m3 copies of the streamed tiles, read row-major as operands
+// of the e4m3 matrix core (the bf16 copies above serve the transposed reads)
+__shared__ __attribute__((aligned(16))) char gA8[2 * kTileB8];
+__shared__ __attribute__((aligned(16))) char gB8[2 * kTileB8];
+__shared__ __attribute__((aligned(16))) char gVk8[kBM * kRowB8];  // dK/dV kernel: V rows of its 256 keys as codes
 
 // 16 consecutive rows map to 16 distinct chunks (row-major reads), and each
 // aligned group of 4 rows differs in bits 3:2 (transposed reads of 4 chunks).
 __device__ __forceinline__ int uswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Rows of e4m3 codes (128 bytes, eight 16-byte chunks): chunk c of row r sits
+// at slot c ^ ((r >> 1) & 7).  Rows r and r + 1 share a 256-byte bank line, so
+// the 16 rows that a 16-lane group of ds_read_b128 reads at one chunk cover
+// all 64 banks.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+// Operand of v_mfma_*_32x32x64_f8f6f4 from an e4m3 tile read row-major: row
+// l32, bytes 64 kk + 32 hl .. + 31.  Both operands of a product take the same
+// pairing (byte e of lane half h is element 64 kk + 32 h + e of the row).
+__device__ __forceinline__ intx8 frag8_rows(const char* t, int l32, int hl, int kk) {
+  const char* r = t + l32 * kRowB8;
+  const uint4 lo = *(const uint4*)(r + ((4 * kk + 2 * hl) ^ swz8(l32)) * 16);
+  const uint4 hi = *(const uint4*)(r + ((4 * kk + 2 * hl + 1) ^ swz8(l32)) * 16);
+  return intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// The same operand for a row the lane reads from global memory.
+__device__ __forceinline__ intx8 frag8_global(const char* row, int hl, int kk) {
+  const uint4 lo = *(const uint4*)(row + 64 * kk + 32 * hl);
+  const uint4 hi = *(const uint4*)(row + 64 * kk + 32 * hl + 16);
+  return intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// A thread's 8 codes (elements 8 lslot .. + 7 of row lrow) into an e4m3 tile.
+__device__ __forceinline__ void stash8(char* t, int lrow, int lslot, uint2 c) {
+  *(uint2*)(t + lrow * kRowB8 + ((lslot >> 1) ^ swz8(lrow)) * 16 + (lslot & 1) * 8) = c;
+}
 
 // Two e4m3 codes (bytes 2*hi, 2*hi + 1 of w) as two bf16 values.  An e4m3
 // value has at most 4 significant bits and an exponent within bf16's range,

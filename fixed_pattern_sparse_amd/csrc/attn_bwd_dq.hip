@@ -50,20 +50,40 @@ attn_bwd_dq_kernel(const AttnArgs a) {
   const bool qok = jq < n;
   const int tq = rows.tok(jq);
   const int64_t qoff = (int64_t)tq * rs;
-  bf16x8 qf[KK], dof[KK];
+  bf16x8 qf[KK], dof[KK];   // bf16 path
+  intx8 qf8[2], dof8[2];     // 8-bit path: codes for the e4m3 matrix core
+  if constexpr (F8) {
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    qf[kk] = as_bf16x8(load8<F8>(qb, qoff + kk * 16 + hl * 8));
-    dof[kk] = as_bf16x8(load8<F8>(dob, qoff + kk * 16 + hl * 8));
-    __asm__ volatile("" : "+v"(qf[kk]), "+v"(dof[kk]));
+    for (int kk = 0; kk < 2; ++kk) {
+      qf8[kk] = frag8_global(qb + qoff, hl, kk);
+      dof8[kk] = frag8_global(dob + qoff, hl, kk);
+      __asm__ volatile("" : "+v"(qf8[kk]), "+v"(dof8[kk]));
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qf[kk] = as_bf16x8(load8<F8>(qb, qoff + kk * 16 + hl * 8));
+      dof[kk] = as_bf16x8(load8<F8>(dob, qoff + kk * 16 + hl * 8));
+      __asm__ volatile("" : "+v"(qf[kk]), "+v"(dof[kk]));
+    }
   }
   const int64_t ridx = ((int64_t)wi.b * N + tq) * a.heads + wi.head;
   const float lse2 = a.lse[ridx] * kLog2e;
   const float dq_d = a.dsum[ridx];
   const float c = F8 ? a.scale_log2 * a.descale[1] * a.descale[3] : a.scale_log2;
 
-  *(uint4*)(gA + lrow * kRowB + sw_st) = widen8<F8>(kx);
-  *(uint4*)(gB + lrow * kRowB + sw_st) = widen8<F8>(vx);
+  // K and V of a key tile: the 8-bit path keeps their codes for the e4m3
+  // products and a bf16 copy of K for the transposed reads of dQ's product
+  auto stash = [&](int buf) {
+    *(uint4*)(gA + buf * kTileB + lrow * kRowB + sw_st) = widen8<F8>(kx);
+    if constexpr (F8) {
+      stash8(gA8 + buf * kTileB8, lrow, lslot, kx);
+      stash8(gB8 + buf * kTileB8, lrow, lslot, vx);
+    } else {
+      *(uint4*)(gB + buf * kTileB + lrow * kRowB + sw_st) = vx;
+    }
+  };
+  stash(0);
   __syncthreads();
 
   floatx16 acc[DB];
@@ -75,12 +95,23 @@ attn_bwd_dq_kernel(const AttnArgs a) {
     const bool more = j + 1 < nkv;
     if (more) fetch(j + 1, kx, vx);
     const char* sK = gA + buf * kTileB;
-    const char* sV = gB + buf * kTileB;
     floatx16 s = floatx16{}, dp = floatx16{};
+    if constexpr (F8) {
+      // S^T = K^ Q^T and dP^T = V^ dO^T on the codes (e4m3 matrix core)
+      const char* sK8 = gA8 + buf * kTileB8;
+      const char* sV8 = gB8 + buf * kTileB8;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sK, l32, hl, kk), qf[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sV, l32, hl, kk), dof[kk], dp, 0, 0, 0);
+      for (int kk = 0; kk < 2; ++kk) {
+        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag8_rows(sK8, l32, hl, kk), qf8[kk], s, 0, 0, 0, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag8_rows(sV8, l32, hl, kk), dof8[kk], dp, 0, 0, 0, 0, 0, 0);
+      }
+    } else {
+      const char* sV = gB + buf * kTileB;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sK, l32, hl, kk), qf[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows(sV, l32, hl, kk), dof[kk], dp, 0, 0, 0);
+      }
     }
     // dS^T = P^T * (dP^T - D); keys past the end of the subsequence get P = 0
     float ds[16];
@@ -98,10 +129,7 @@ attn_bwd_dq_kernel(const AttnArgs a) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols(sK, lane, hl, db, cc), dsb[cc], acc[db], 0, 0, 0);
-    if (more) {
-      *(uint4*)(gA + (buf ^ 1) * kTileB + lrow * kRowB + sw_st) = widen8<F8>(kx);
-      *(uint4*)(gB + (buf ^ 1) * kTileB + lrow * kRowB + sw_st) = widen8<F8>(vx);
-    }
+    if (more) stash(buf ^ 1);
     __syncthreads();
   }
   const float mul = F8 ? a.scale * a.descale_do[1] * a.descale[5] * a.descale[3] : a.scale;

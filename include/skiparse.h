@@ -238,9 +238,9 @@ int skiparse_attn_fwd_lse_fp8(const skiparse_plan* plan, const void* q8, const v
 /*
  * Backward pass on e4m3 inputs: skiparse_attn_bwd's gradients of the
  * dequantized tensors Q = q8 / s_q, K = k8 / s_k, V = v8 / s_v for the
- * dequantized upstream gradient dO = dout8 / s_do.  Every product of two
- * codes is exact and accumulates in fp32, as on the 8-bit matrix core; P and
- * dS enter their products as bf16.
+ * dequantized upstream gradient dO = dout8 / s_do.  The products of two
+ * coded tensors (S = Q K^T and dP = dO V^T) run on the e4m3 matrix core; P
+ * and dS enter the products for dV, dK and dQ as bf16, against the codes.
  *   q8, k8, v8, dev_descale_qkv   as in skiparse_attn_fwd_lse_fp8
  *   o, lse             the bf16 output and log-sum-exp of the forward (for
  *                      example skiparse_attn_fwd_lse_fp8 with the same scale)
