@@ -113,12 +113,14 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
     qx = load_raw8<F8>(qb, e);
     dx = load_raw8<F8>(db_, e);
     if (lslot == 0) {
+      // raw L and D of the row: they are scaled only when stored, after the
+      // tile's compute, so their latency stays hidden like that of the rows
       const int64_t ridx = ((int64_t)wi.b * N + t) * a.heads + wi.head;
-      ln = j < n ? -(a.lse[ridx] * kLog2e) * inv_c : -INFINITY;
-      dn = j < n ? -a.dsum[ridx] : 0.f;
+      ln = a.lse[ridx];
+      dn = a.dsum[ridx];
     }
   };
-  auto stash = [&](int buf, const Raw8<F8>& qx, const Raw8<F8>& dx, float ln, float dn) {
+  auto stash = [&](int buf, int tile, const Raw8<F8>& qx, const Raw8<F8>& dx, float ln, float dn) {
     *(uint4*)(gA + buf * kTileB + lrow * kRowB + sw_st) = widen8<F8>(qx);
     *(uint4*)(gB + buf * kTileB + lrow * kRowB + sw_st) = widen8<F8>(dx);
     if constexpr (F8) {   // codes for the e4m3 products S and dP
@@ -126,8 +128,9 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
       stash8(gB8 + buf * kTileB8, lrow, lslot, dx);
     }
     if (lslot == 0) {
-      gL[buf * kBT + lrow] = ln;
-      gDn[buf * kBT + lrow] = dn;
+      const bool ok = tile * kBT + lrow < n;
+      gL[buf * kBT + lrow] = ok ? -(ln * kLog2e) * inv_c : -INFINITY;
+      gDn[buf * kBT + lrow] = ok ? -dn : 0.f;
     }
   };
   Raw8<F8> qx, dx;
@@ -166,7 +169,7 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
   const char* sVk = gVk + wave * 32 * kRowB;     // the wave's 32 key rows
   const char* sVk8 = gVk8 + wave * 32 * kRowB8;  // the same as codes (8-bit path)
 
-  stash(0, qx, dx, ln, dn);
+  stash(0, 0, qx, dx, ln, dn);
   __syncthreads();
 
   floatx16 accK[DB], accV[DB];
@@ -243,7 +246,7 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
         accK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols(sQ, lane, hl, db, cc), dsb[cc], accK[db], 0, 0, 0);
-    if (more) stash(buf ^ 1, qx, dx, ln, dn);
+    if (more) stash(buf ^ 1, j + 1, qx, dx, ln, dn);
     __syncthreads();
   }
   if (kok) {
