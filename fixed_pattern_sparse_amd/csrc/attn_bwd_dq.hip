@@ -69,7 +69,10 @@ attn_bwd_dq_kernel(const AttnArgs a) {
   }
   const int64_t ridx = ((int64_t)wi.b * N + tq) * a.heads + wi.head;
   const float lse2 = a.lse[ridx] * kLog2e;
-  const float dq_d = a.dsum[ridx];
+  float dq_d = a.dsum[ridx];
+  // wait for D here: its first use is inside the key loop, where the wait
+  // for it would cover the next tile's prefetch too, on every iteration
+  __asm__ volatile("" : "+v"(dq_d));
   const float c = F8 ? a.scale_log2 * a.descale[1] * a.descale[3] : a.scale_log2;
 
   // K and V of a key tile: the 8-bit path keeps their codes for the e4m3
