@@ -20,10 +20,18 @@ Bars.
   and the oracle forms the row term of dS from that same O (rowsum(dO * O),
   pinned against the Jacobian form), since a dequantized e4m3 V is in general
   no bf16 value and a one-member subsequence would otherwise show the
-  rounding of O as a gradient that should be zero.  Every product of two
-  codes is exact (bf16 MFMA on the widened codes) and accumulates in fp32; P
-  and dS enter their products as bf16, as in the bf16 backward pass, so its
-  bar applies: max|g - g_ref| <= 2e-2 * max|g_ref| per tensor.
+  rounding of O as a gradient that should be zero.  S and dP, the products
+  of two coded tensors, run on the e4m3 matrix core with the truncation
+  above: a score moves by at most 2^-11 * M_i, which changes P by at most
+  ln 2 times that relatively, and dP by at most 2^-11 * sum_d |dO_d V_jd|.
+  That worst case is 0.4% for the plain inputs here and 4% for the ones with
+  outlier channels (M_i up to 127); the truncation of a group's products
+  follows their signs, so in practice it largely cancels.  dV, dK and dQ take
+  P and dS as bf16 against exact bf16 copies of the codes, with fp32
+  accumulation, as in the bf16 backward pass, whose bar is kept:
+  max|g - g_ref| <= 2e-2 * max|g_ref| per tensor.  Measured on MI355X: 2.6e-3
+  to 6.5e-3 on every shape, outliers included, except the one-token case,
+  whose dQ and dK are zero in exact arithmetic (1.1e-2 of the 1e-3 floor).
 * Chained (the kernels' own forward output and log-sum-exp feed the
   backward): D = rowsum(dO * O) takes the 8-bit forward's output, whose P
   went through e4m3, so the gradients inherit that forward's error; the bar is
@@ -142,8 +150,11 @@ def test_bwd_fp8_small(shp, kf, mode, outl):
     grads = [torch.empty(shp, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
     sk.skiparse_attn_bwd_fp8(plan, *codes, scales, o_in, do8, dscale, lse_in, *grads)
     torch.cuda.synchronize()
-    for name, g, w in zip(("dq", "dk", "dv"), grads, (dq_w, dk_w, dv_w)):
-        assert rel_err(np64(g), w) <= TOL, name
+    errs = {name: rel_err(np64(g), w) for name, g, w in zip(("dq", "dk", "dv"), grads, (dq_w, dk_w, dv_w))}
+    print(f"\n[8-bit backward] {shp} k={kf} mode={mode} outliers={outl}: " +
+          ", ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for name, e in errs.items():
+        assert e <= TOL, name
 
 
 @pytest.mark.parametrize("shp,kf,mode,outl", SMALL[:4])
