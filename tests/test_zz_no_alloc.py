@@ -58,3 +58,45 @@ def test_noalloc_argument_errors():
     assert _noalloc(x, y, s, x_dtype=7) == sk.EINVAL
     assert _noalloc(x, y, s, fp8_max=0.0) == sk.EINVAL
     assert _noalloc(x, x.view(torch.uint8)[:64], s) == sk.EINVAL          # y overlaps x
+
+
+def test_noalloc_under_graph_capture():
+    """The callers it is for: quantization of Q, K, V through the shared
+    scratch and the e4m3 attention, captured in one graph and replayed three
+    times.  Between replays an eager call quantizes another tensor through the
+    same scratch; every replay must still equal the eager result bit for bit
+    (each call writes every partial maximum it reads)."""
+    shp = (1, 3, 13, 22, 2, 128)
+    q, k, v = (torch.from_numpy(wl.normal_tensor(shp, 1201, i)).to(torch.bfloat16).to(DEV) for i in range(3))
+    plan = sk.skiparse_plan_init(*shp, 2, sk.MODE_GROUP)
+    codes = [torch.empty(shp, dtype=torch.uint8, device=DEV) for _ in range(3)]
+    scales = torch.empty((3, 2), dtype=torch.float32, device=DEV)
+    o = torch.empty_like(q)
+
+    def run(stream=None):
+        for t, c_, i in zip((q, k, v), codes, range(3)):
+            sk.skiparse_quant_fp8_noalloc(t, c_, scales[i], stream=stream)   # raises on an error code
+        sk.skiparse_attn_fwd(plan, sk.FP8_E4M3, *codes, o, descale_qkv=scales, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    want = [o.clone(), scales.clone()] + [c_.clone() for c_ in codes]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run(s)
+    other = torch.from_numpy(wl.normal_tensor((1, 1, 1, 1, 1, 3 * 2**20 + 5), 1202, 0) * np.float32(50.0)).to(DEV)
+    oy = torch.empty(other.numel(), dtype=torch.uint8, device=DEV)
+    osc = torch.empty(2, dtype=torch.float32, device=DEV)
+    for rep in range(3):
+        for t in [o, scales]:
+            t.fill_(float("nan"))
+        for c_ in codes:
+            c_.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip([o, scales] + codes, want):
+            assert torch.equal(got, exp), f"replay {rep} differs from the eager result"
+        assert _noalloc(other, oy, osc) == sk.OK     # overwrites the scratch between replays
+        torch.cuda.synchronize()
