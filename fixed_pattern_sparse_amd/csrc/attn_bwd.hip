@@ -30,9 +30,10 @@
 // from e4m3 copies of the staged tiles and code fragments in registers; the
 // transposed operands of dV, dK and dQ come from bf16 copies, widened from the
 // codes at staging (exact: every e4m3 value is a bf16 value), against P and dS
-// in bf16.  The descales fold into scalars: the exp2 constant takes 1/(s_q s_k), D enters as D / f with
-// f = 1/(s_do s_v) so dP - D is f (dO^ V^T - D/f), and the outputs take
-// scale f / s_k (dQ), scale f / s_q (dK) and 1/s_do (dV).
+// in bf16.  The descales fold into scalars: the exp2 constant takes
+// 1/(s_q s_k), D enters as D / f with f = 1/(s_do s_v) so dP - D is
+// f (dO^ V^T - D/f), and the outputs take scale f / s_k (dQ), scale f / s_q
+// (dK) and 1/s_do (dV).
 // Per-query L and D enter the dK/dV kernel through the MFMA accumulator's
 // initial value, so they cost no registers of their own.  Each staged tile is
 // read both row-major (ds_read_b128, 16 rows at one chunk) and transposed
@@ -138,7 +139,8 @@ attn_bwd_dkv_fused_kernel(const AttnArgs a) {
   fetch(0, qx, dx, ln, dn);
 
   // V rows of the work-group's 256 keys (clamped past the end), swizzled like
-  // the tiles: key row r at chunk c ^ uswz(r)
+  // the tiles: key row r at chunk c ^ uswz(r) in bf16, or as codes at slot
+  // c ^ swz8(r) on the 8-bit path (V only enters dP, read row-major)
   const int key0 = wi.qtile * kBM;
 #pragma unroll
   for (int i = 0; i < kBM * kCH / kThreads; ++i) {
