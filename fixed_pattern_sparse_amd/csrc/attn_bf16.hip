@@ -74,8 +74,11 @@ struct Layout {
 // work-group (n <= kTokCap); 1: a walker over the (t, h') row and w' column
 // tables (table room needed); these use 32-bit offsets from a scalar base
 // (T*H*W < 2^24, heads*d*2 < 2^24, a batch sample's tensor < 4 GB).  0: the
-// index function per row.
-template <int D, int ROWS>
+// index function per row.  LSE: the call keeps the log-sum-exp (the training
+// forward); its denominator then also sums the unrounded p in fp32, so the
+// log-sum-exp is exact up to fp32, while O is normalized by the same
+// bf16-rounded sum as without it (the two outputs are identical).
+template <int D, int ROWS, bool LSE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const AttnArgs a) {
   using L = Layout<D>;
@@ -179,6 +182,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = floatx16{};
   float m_run = -INFINITY, l_run = 0.f;
+  float l_exact = 0.f;   // LSE only: sum of the unrounded p
   const float c = a.scale_log2;
 
   // One tile.  BUF (the LDS buffer holding the tile) and LAST (the final tile:
@@ -234,10 +238,11 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     // max is taken only when some p could exceed kBig (the partial sum of a
     // lane bounds each of its terms), which also covers the first tile
     bf16x8 pk[2][2];
-    float lsum;
+    float lsum, lsum_exact;
     auto exps = [&]() {
       const float mneg = -m_run;
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      float le[4] = {0.f, 0.f, 0.f, 0.f};
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -251,10 +256,12 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
             // terms per dot2 instruction
             bf16x2 pp = {(__bf16)p0, (__bf16)p1};
             ls[mb * 2 + cc] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[mb * 2 + cc], false);
+            if constexpr (LSE) le[mb * 2 + cc] += p0 + p1;
             pk[mb][cc][2 * e] = pp[0];
             pk[mb][cc][2 * e + 1] = pp[1];
           }
       lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      if constexpr (LSE) lsum_exact = (le[0] + le[1]) + (le[2] + le[3]);
     };
     exps();
     if (__builtin_amdgcn_ballot_w64(!(lsum <= kBig))) {
@@ -270,6 +277,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
       m_run = mnew;
       l_run *= alpha;
+      if constexpr (LSE) l_exact *= alpha;
       // an fma with a zero addend, not a multiply: this keeps the compiler
       // from folding the rare rescale into an every-tile multiply
 #pragma unroll
@@ -279,6 +287,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
       exps();
     }
     l_run += lsum;
+    if constexpr (LSE) l_exact += lsum_exact;
 
     // O^T += V^T P^T; V fragments are read one step ahead of their MFMA
     auto vfrag = [&](int step) -> bf16x8 {   // step = (db * 2 + mb) * 2 + cc
@@ -335,11 +344,16 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   const float inv = 1.0f / l_tot;
-  if (a.lse != nullptr && qok && hl == 0) {
+  if constexpr (LSE) {
     // both lane halves hold the same running max; log of the denominator in
-    // natural units: ln 2 * (m + log2 l), m being in log2 units of s*scale
-    const int64_t N = (int64_t)a.g.T * a.g.H * a.g.W;
-    a.lse[((int64_t)b * N + tokq) * a.heads + head] = 0.69314718055994531f * (m_run + __log2f(l_tot));
+    // natural units: ln 2 * (m + log2 l), m being in log2 units of s*scale and
+    // l the sum of the unrounded p
+    const auto swe = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_exact), __float_as_uint(l_exact), false, false);
+    const float le_tot = __uint_as_float(swe[0]) + __uint_as_float(swe[1]);
+    if (qok && hl == 0) {
+      const int64_t N = (int64_t)a.g.T * a.g.H * a.g.W;
+      a.lse[((int64_t)b * N + tokq) * a.heads + head] = 0.69314718055994531f * (m_run + __log2f(le_tot));
+    }
   }
   if (qok) {
 #pragma unroll
@@ -354,27 +368,28 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool LSE>
 hipError_t launch_d(AttnArgs a, int B, hipStream_t stream) {
   assign_tiles(a, B, kBM);
   if (a.total_tiles == 0) return hipSuccess;
   const int64_t row_bytes = (int64_t)a.row_stride * 2;
   if (a.g.kh == 1 && a.g.kw == 1 && offsets32_ok(a, row_bytes))
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 3>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 3, LSE>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
   else if (token_table_ok(a, row_bytes, kTokCap))
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2, LSE>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
   else if (fast_rows_ok(a, row_bytes))
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1, LSE>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 0>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 0, LSE>), dim3(a.total_tiles), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(AttnArgs a, int B, int d, hipStream_t stream) {
-  if (d == 128) return launch_d<128>(a, B, stream);
-  return launch_d<64>(a, B, stream);
+  const bool lse = a.lse != nullptr;
+  if (d == 128) return lse ? launch_d<128, true>(a, B, stream) : launch_d<128, false>(a, B, stream);
+  return lse ? launch_d<64, true>(a, B, stream) : launch_d<64, false>(a, B, stream);
 }
 
 }  // namespace skiparse

@@ -2,12 +2,14 @@
 pass (dQ, dK, dV) through the C ABI, against the oracle's float64 gradients
 (oracle/skiparse_bwd.py) on the same bf16 inputs.
 
-Bars.  Log-sum-exp: within 2^-8 (absolute, natural log): the kernel's
-denominator sums the bf16-rounded weights its PV product uses, each within
-2^-8 relative of the exact one (bf16 keeps 8 significant bits, so rounding to
-nearest moves a value by at most 2^-8 of it), so log l is within 2^-8 of the
-exact value; the scores themselves are exact products of the bf16 inputs
-accumulated in fp32.  Gradients: max|g - g_ref| <= 2e-2 * max|g_ref| per tensor, the
+Bars.  Log-sum-exp: within 2e-4 (absolute, natural log).  When it keeps the
+log-sum-exp the kernel sums the unrounded exponentials in fp32 beside the
+bf16-rounded ones that normalize O (so O is the same as without it), and
+the scores are exact products of the bf16 inputs accumulated in fp32: the
+error is that of fp32 accumulation and of v_exp_f32 (about 1e-5 at the
+tested sizes, a few hundred sequential additions of 2^-24 each at most),
+far inside the bar, while a wrong scale, offset or dropped tile moves it by
+far more.  Gradients: max|g - g_ref| <= 2e-2 * max|g_ref| per tensor, the
 bf16 bar taken relative to the tensor's largest entry (gradients are often
 well below 1, where a max(1, .) normalisation would not test anything).  The
 kernels see the bf16 output O of the forward pass, the oracle the exact one;
@@ -29,7 +31,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 TOL = 2e-2
-LSE_TOL = 2.0 ** -8
+LSE_TOL = 2e-4
 
 
 def check_lse(got, q, k, kf, mode):

@@ -4,7 +4,7 @@ group-wise, and the two Skiparse-1D rules), k from 1 to 8, ragged H and W
 2.  Each case is compared element by element with the oracle on four paths,
 at the bars the other tests derive: the bf16 forward (2e-2 of max(1, max|O|)),
 the e4m3 forward on the oracle's own quantization (codes and scales bit for
-bit, 6e-2), the bf16 training forward and backward (log-sum-exp within 2^-8,
+bit, 6e-2), the bf16 training forward and backward (log-sum-exp within 2e-4,
 gradients within 2e-2 of each tensor's largest entry), and the 8-bit backward
 given the oracle's output and log-sum-exp (2e-2, the row term of dS formed
 from that same output)."""
@@ -85,7 +85,7 @@ def test_sweep(shp, kf, mode):
     torch.cuda.synchronize()
     assert torch.equal(o, out)
     np.testing.assert_allclose(lse.cpu().numpy().astype(np.float64), bwd.attention_lse(q64, k64, kf, mode),
-                               rtol=0, atol=2.0 ** -8)
+                               rtol=0, atol=2e-4)
     for g, w in zip(grads, bwd.skiparse_attention_bwd(q64, k64, v64, do64, kf, mode)):
         assert rel_grad(np64(g), w) <= 2e-2
 
