@@ -28,8 +28,8 @@ class HashRows:
     """The (B, N, heads, d) view of a hash tensor that the oracle indexes with
     [b, token indices, head]; rows are formed on demand."""
 
-    def __init__(self, tensor_id, gain):
-        B, T, H, W, nh, d = SHAPE
+    def __init__(self, tensor_id, gain, shape=SHAPE):
+        B, T, H, W, nh, d = shape
         self.shape = (B, T * H * W, nh, d)
         self.t, self.gain = tensor_id, gain
 
@@ -133,3 +133,53 @@ def test_fp8_past_32bit_offsets():
     assert np.max(np.abs(want)) > 0.05
     err = np.max(np.abs(got - want)) / max(1.0, np.max(np.abs(want)))
     assert err <= 6e-2, err
+
+
+# The training path past the same limit with many heads instead of many
+# tokens: 2^19 tokens of 64 heads (16 KB per token), 8 GiB per tensor, so byte
+# offsets within a sample reach 2^33 while the oracle's key gradients stay
+# cheap (8192-member subsequences at k = 8).  The training forward, dQ and
+# dK/dV all take the index-function row source with 64-bit offsets here.
+BWD_SHAPE = (1, 2, 512, 512, 64, 128)
+BWD_GAIN = (4.0, 4.0, 1.0, 1.0)     # Q, K, V, dO
+
+
+def test_bwd_past_32bit_offsets():
+    """dQ, dK, dV of sampled rows (the first and the last subsequence, which
+    holds the tensor's last token; the first and the last head) against the
+    oracle's float64 gradients, at the bf16 backward's bar (2e-2 of each
+    tensor's largest sampled entry)."""
+    from oracle import skiparse_bwd as bwd
+    mode = sk.MODE_TOKEN
+    B, T, H, W, nh, d = BWD_SHAPE
+    N = T * H * W
+    assert N * nh * d * 2 > 1 << 32
+    q, k, v, do = (wl.hash_fill_(torch.empty(BWD_SHAPE, dtype=torch.bfloat16, device="cuda"), i, BWD_GAIN[i])
+                   for i in range(4))
+    out, lse = sk.attention_train(q, k, v, KF, mode)
+    dq, dk, dv = sk.attention_bwd(q, k, v, out, do, lse, KF, mode)
+    torch.cuda.synchronize()
+    del q, k, v, do, out, lse
+    members = ref.subsequence_members(T, H, W, KF, mode)
+    rows = [HashRows(i, BWD_GAIN[i], BWD_SHAPE) for i in range(4)]
+    rng = np.random.default_rng(9)
+    worst = 0.0
+    for h in (0, nh - 1):
+        toks = []
+        for s in (0, len(members) - 1):
+            mem = members[s]
+            toks += [int(mem[0]), int(mem[-1])] + [int(x) for x in rng.choice(mem, 2, replace=False)]
+        toks = np.array(sorted(set(toks)), np.int64)
+        assert toks[-1] == N - 1
+        sel = torch.from_numpy(toks).cuda()
+        got = [g.view(B, N, nh, d)[0, sel, h].float().cpu().numpy().astype(np.float64) for g in (dq, dk, dv)]
+        want = [bwd.dq_rows(*rows, T, H, W, KF, mode, 0, h, toks)]
+        want += list(bwd.dkv_rows(*rows, T, H, W, KF, mode, 0, h, toks))
+        for name, g_, w_ in zip(("dq", "dk", "dv"), got, want):
+            scale = np.max(np.abs(w_))
+            assert scale > 1e-3, name                     # a gradient worth checking
+            worst = max(worst, np.max(np.abs(g_ - w_)) / scale)
+    del dq, dk, dv
+    torch.cuda.empty_cache()
+    print(f"\n[64-bit backward] worst error {worst:.3e} of each gradient's largest sampled entry")
+    assert worst <= TOL, worst
