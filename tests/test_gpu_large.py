@@ -85,8 +85,8 @@ class DequantRows(HashRows):
     """Rows of a hash tensor after per-tensor e4m3 quantization with the
     oracle's codec at the scale 448 / (amax + 1e-12), amax = 0.5 * gain."""
 
-    def __init__(self, tensor_id, gain):
-        super().__init__(tensor_id, gain)
+    def __init__(self, tensor_id, gain, shape=SHAPE):
+        super().__init__(tensor_id, gain, shape)
         from oracle import fp8_ref as f8
         self.f8 = f8
         self.scale = f8.per_tensor_scale(np.float32(0.5 * gain))
@@ -182,4 +182,63 @@ def test_bwd_past_32bit_offsets():
     del dq, dk, dv
     torch.cuda.empty_cache()
     print(f"\n[64-bit backward] worst error {worst:.3e} of each gradient's largest sampled entry")
+    assert worst <= TOL, worst
+
+
+def test_bwd_fp8_past_32bit_offsets():
+    """The 8-bit backward on the same shape, on the e4m3 codes of Q, K, V and
+    dO (each amax is 0.5 * gain exactly, from the generator), all on 64-bit
+    offsets.  As in the small 8-bit tests, the backward alone is checked: the
+    forward's output and log-sum-exp rows of the sampled subsequences are
+    replaced by the oracle's (O rounded to bf16), so the bar is the bf16
+    backward's 2e-2; the chained step's extra error from the e4m3 forward is
+    covered by the sampled 720P-5s test."""
+    from oracle import skiparse_bwd as bwd
+    mode = sk.MODE_GROUP
+    B, T, H, W, nh, d = BWD_SHAPE
+    N = T * H * W
+    numel = N * nh * d
+    assert numel * 2 > 1 << 32
+    for i in range(4):
+        assert exact_amax_index(i, numel) is not None
+    q, k, v, do = (wl.hash_fill_(torch.empty(BWD_SHAPE, dtype=torch.bfloat16, device="cuda"), i, BWD_GAIN[i])
+                   for i in range(4))
+    out, lse, codes, scales = sk.attention_train_fp8(q, k, v, KF, mode)
+    del q, k, v
+    members = ref.subsequence_members(T, H, W, KF, mode)
+    rows = [DequantRows(i, BWD_GAIN[i], BWD_SHAPE) for i in range(4)]
+    h = nh // 2
+    subs = (0, len(members) - 1)
+    for s in subs:                                   # the oracle's O and log-sum-exp for these rows
+        mem = members[s]
+        qq, kk, vv = (r[0, mem, h] for r in rows[:3])
+        sc = (qq @ kk.T) / np.sqrt(d)
+        m = sc.max(axis=1, keepdims=True)
+        e = np.exp(sc - m)
+        z = e.sum(axis=1, keepdims=True)
+        sel = torch.from_numpy(mem).cuda()
+        out.view(B, N, nh, d)[0, sel, h] = torch.from_numpy(((e / z) @ vv).astype(np.float32)).to(torch.bfloat16).cuda()
+        lse.view(B, N, nh)[0, sel, h] = torch.from_numpy((m + np.log(z))[:, 0].astype(np.float32)).cuda()
+    dq, dk, dv = sk.attention_bwd_fp8(codes, scales, out, do, lse, KF, mode)
+    torch.cuda.synchronize()
+    del do, out, lse, codes, scales
+    rng = np.random.default_rng(10)
+    toks = []
+    for s in subs:
+        mem = members[s]
+        toks += [int(mem[0]), int(mem[-1])] + [int(x) for x in rng.choice(mem, 2, replace=False)]
+    toks = np.array(sorted(set(toks)), np.int64)
+    assert toks[-1] == N - 1
+    sel = torch.from_numpy(toks).cuda()
+    got = [g.view(B, N, nh, d)[0, sel, h].float().cpu().numpy().astype(np.float64) for g in (dq, dk, dv)]
+    want = [bwd.dq_rows(*rows, T, H, W, KF, mode, 0, h, toks)]
+    want += list(bwd.dkv_rows(*rows, T, H, W, KF, mode, 0, h, toks))
+    worst = 0.0
+    for name, g_, w_ in zip(("dq", "dk", "dv"), got, want):
+        scale = np.max(np.abs(w_))
+        assert scale > 1e-3, name
+        worst = max(worst, np.max(np.abs(g_ - w_)) / scale)
+    del dq, dk, dv
+    torch.cuda.empty_cache()
+    print(f"\n[64-bit 8-bit backward] worst error {worst:.3e} of each gradient's largest sampled entry")
     assert worst <= TOL, worst
