@@ -399,6 +399,14 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _check_out(out, shape, dtype, device):
+    """A caller's output tensor must be exactly what the kernels write:
+    contiguous, of the given shape and dtype, on the inputs' device."""
+    if (tuple(out.shape) != tuple(shape) or out.dtype != dtype or not out.is_contiguous()
+            or out.device != device):
+        raise ValueError(f"out must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
+
+
 def attention(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, descale_qkv=None, out=None,
               sub_begin: int = 0, sub_count: int = 0, plan: SkiparsePlan | None = None):
     """Skiparse-2D attention forward on (B, T, H, W, heads, d) device tensors."""
@@ -412,9 +420,11 @@ def attention(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, descale_q
     code = _dtype_code(q)
     if plan is None:
         plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
+    odt = torch.float32 if code == F32 else torch.bfloat16
     if out is None:
-        odt = torch.float32 if code == F32 else torch.bfloat16
         out = torch.empty(q.shape, dtype=odt, device=q.device)
+    else:
+        _check_out(out, q.shape, odt, q.device)
     skiparse_attn_fwd(plan, code, q, k, v, out, softmax_scale, descale_qkv, sub_begin, sub_count)
     return out
 
@@ -424,7 +434,11 @@ def quantize_fp8(x, fp8_max: float = 448.0, eps: float = 1e-12, scale_out=None):
     ``scale_out`` (2 fp32 on the device) receives {scale, 1/scale} if given."""
     import torch
     y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    sc = torch.empty(2, dtype=torch.float32, device=x.device) if scale_out is None else scale_out
+    if scale_out is None:
+        sc = torch.empty(2, dtype=torch.float32, device=x.device)
+    else:
+        _check_out(scale_out, (2,), torch.float32, x.device)
+        sc = scale_out
     skiparse_quant_fp8(x.contiguous(), y, sc, fp8_max, eps)
     return y, sc
 
@@ -553,7 +567,11 @@ class BlockFP8:
         if self._ws is None or self._ws.numel() < need:
             self._ws = None
             self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
-        y = torch.empty_like(x) if out is None else out
+        if out is None:
+            y = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+        else:
+            _check_out(out, x.shape, torch.bfloat16, x.device)
+            y = out
         skiparse_block_fwd_fp8(plan, x, self.w_codes, self.w_scales, y, self.rope_theta, self.rope_dims, self._ws)
         return y
 

@@ -382,3 +382,25 @@ def test_gemm_argument_errors():
     assert call(w=None) == sk.EINVAL
     assert call(y=0x10000 + 64) == sk.EINVAL               # y overlaps x
     assert sk.skiparse_last_error()
+
+
+def test_wrappers_reject_mismatched_outputs():
+    """A caller's output tensor is checked before any kernel could write past
+    it: shape, dtype, layout and device must be exactly what the kernels write
+    (the checks run on the host, so CPU tensors reach them)."""
+    import torch
+    shp = (1, 2, 4, 6, 2, 64)
+    q = torch.zeros(shp, dtype=torch.bfloat16)
+    good = torch.empty(shp, dtype=torch.bfloat16)
+    for bad in (torch.empty((1, 2, 4, 6, 2, 32), dtype=torch.bfloat16),          # shape
+                torch.empty(shp, dtype=torch.float32),                           # dtype
+                torch.empty((64, 2, 6, 4, 2, 1), dtype=torch.bfloat16).permute(5, 4, 3, 2, 1, 0)):  # layout
+        with pytest.raises(ValueError, match="out must be"):
+            sk.attention(q, q, q, 2, sk.MODE_TOKEN, out=bad)
+    sk._check_out(good, shp, torch.bfloat16, q.device)
+    x = torch.zeros((1, 2, 4, 6, 256), dtype=torch.bfloat16)
+    blk = sk.BlockFP8(None, None, heads=2, kf=2, mode=sk.MODE_TOKEN)
+    with pytest.raises(ValueError, match="out must be"):
+        blk(x, out=torch.empty((1, 2, 4, 6, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        sk.quantize_fp8(q, scale_out=torch.empty(3, dtype=torch.float32))
