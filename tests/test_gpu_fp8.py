@@ -97,3 +97,16 @@ def test_fp8_workload_sampled(kf, mode):
         worst = max(worst, err_ratio(on[0, toks, h], r))
     print(f"\n[sampled parity] 720p_5s_fp8 k={kf} mode={mode} e4m3: max err {worst:.3e} of max(1, max|O|)")
     assert worst <= TOL, worst
+
+
+@pytest.mark.parametrize("mode", [sk.MODE_TOKEN, sk.MODE_GROUP])
+def test_fp8_repeatable_at_720p(mode):
+    """Three calls of the e4m3 path on the same 720P-5s inputs are
+    bit-identical (302 key tiles per subsequence; see the bf16 check)."""
+    shape = wl.WORKLOADS["720p_5s_fp8"].shape
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1005)
+    q, k, v = (torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16) for _ in range(3))
+    outs = [sk.attention_fp8(q, k, v, 2, mode)[0] for _ in range(3)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])

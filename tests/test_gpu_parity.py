@@ -168,6 +168,25 @@ def test_bf16_deterministic():
     assert torch.equal(a, b)
 
 
+def device_normal(shape, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return [torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16) for _ in range(3)]
+
+
+def test_bf16_repeatable_at_720p():
+    """Three calls on the same 720P-5s inputs are bit-identical.  Each
+    subsequence streams 302 key tiles, so a scheduling or synchronisation
+    defect that shows only on long loops would change the output between
+    calls; the small-shape check above covers four tiles."""
+    shape = wl.WORKLOADS["720p_5s"].shape
+    q, k, v = device_normal(shape, 1001)
+    outs = [sk.attention(q, k, v, 2, mode) for mode in (sk.MODE_TOKEN, sk.MODE_GROUP) for _ in range(3)]
+    torch.cuda.synchronize()
+    for i in (0, 3):
+        assert torch.equal(outs[i], outs[i + 1]) and torch.equal(outs[i], outs[i + 2])
+
+
 # ---------------------------------------------------------------------------
 # bf16 at the workload shapes: sampled rows
 # ---------------------------------------------------------------------------
