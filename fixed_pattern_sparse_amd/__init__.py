@@ -315,7 +315,7 @@ def skiparse_quant_fp8(x, y, scale, fp8_max: float = 448.0, eps: float = 1e-12, 
     same numel); ``scale`` receives {scale, 1/scale} (2 fp32, device)."""
     import torch
     if x_dtype is None:
-        x_dtype = BF16 if x.dtype == torch.bfloat16 else F32
+        x_dtype = _float_code(x)
     numel = x.numel()
     if workspace is None:
         nb = skiparse_quant_fp8_workspace_bytes(numel)
@@ -331,7 +331,7 @@ def skiparse_quant_fp8_noalloc(x, y, scale, fp8_max: float = 448.0, eps: float =
     Calls that overlap in time on one GPU race (one shared scratch per GPU)."""
     import torch
     if x_dtype is None:
-        x_dtype = BF16 if x.dtype == torch.bfloat16 else F32
+        x_dtype = _float_code(x)
     _check(lib().skiparse_quant_fp8_noalloc(_ptr(x), x_dtype, x.numel(), _ptr(y), _ptr(scale), float(fp8_max),
                                             float(eps), _stream(stream)))
     return y
@@ -399,6 +399,37 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _float_code(x):
+    """BF16 or F32 for a tensor the quantizer reads; anything else would be
+    read at the wrong element size."""
+    import torch
+    if x.dtype == torch.bfloat16:
+        return BF16
+    if x.dtype == torch.float32:
+        return F32
+    raise TypeError(f"the quantizer reads bfloat16 or float32, not {x.dtype}")
+
+
+def _check_like(names, tensors, shape, dtype, device):
+    """Inputs a kernel reads at a fixed size: each must have the given shape
+    and dtype and sit on the given device (layout is made contiguous by the
+    caller where it copies)."""
+    for name, t in zip(names, tensors):
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+        if t.device != device:
+            raise ValueError(f"{name} must be on {device}, not {t.device}")
+
+
+def _check_lse(lse, B, N, nh, device):
+    import torch
+    _check_like(("lse",), (lse,), (B, N, nh), torch.float32, device)
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous")
+
+
 def _check_out(out, shape, dtype, device):
     """A caller's output tensor must be exactly what the kernels write:
     contiguous, of the given shape and dtype, on the inputs' device."""
@@ -416,8 +447,15 @@ def attention(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, descale_q
     for t in (q, k, v):
         if not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous")
+    _check_like(("k", "v"), (k, v), q.shape, q.dtype, q.device)
     B, T, H, W, nh, d = q.shape
     code = _dtype_code(q)
+    if code == FP8_E4M3:
+        if descale_qkv is None:
+            raise ValueError("e4m3 inputs need descale_qkv (3 x {scale, 1/scale}, fp32)")
+        _check_like(("descale_qkv",), (descale_qkv,), (3, 2), torch.float32, q.device)
+        if not descale_qkv.is_contiguous():
+            raise ValueError("descale_qkv must be contiguous")
     if plan is None:
         plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
     odt = torch.float32 if code == F32 else torch.bfloat16
@@ -459,8 +497,9 @@ def attention_train(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0, pla
     """Training forward on bf16 (B, T, H, W, heads, d) device tensors: returns
     (out, lse) with lse fp32 (B, T*H*W, heads)."""
     import torch
-    if q.dim() != 6 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one (B, T, H, W, heads, d) shape")
+    if q.dim() != 6:
+        raise ValueError("q must be (B, T, H, W, heads, d)")
+    _check_like(("q", "k", "v"), (q, k, v), q.shape, torch.bfloat16, q.device)
     B, T, H, W, nh, d = q.shape
     if plan is None:
         plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
@@ -476,11 +515,11 @@ def attention_bwd(q, k, v, o, dout, lse, kf: int, mode: int, softmax_scale: floa
                   plan: SkiparsePlan | None = None):
     """Backward pass on bf16 device tensors: returns (dq, dk, dv)."""
     import torch
-    if q.dim() != 6 or any(t.shape != q.shape for t in (k, v, o, dout)):
-        raise ValueError("q, k, v, o and dout must share one (B, T, H, W, heads, d) shape")
-    if any(t.dtype != torch.bfloat16 for t in (q, k, v, o, dout)):
-        raise TypeError("q, k, v, o and dout must be bfloat16")
+    if q.dim() != 6:
+        raise ValueError("q must be (B, T, H, W, heads, d)")
+    _check_like(("q", "k", "v", "o", "dout"), (q, k, v, o, dout), q.shape, torch.bfloat16, q.device)
     B, T, H, W, nh, d = q.shape
+    _check_lse(lse, B, T * H * W, nh, q.device)
     if plan is None:
         plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
     # the kernels write rows in contiguous order, whatever q's strides are
@@ -497,8 +536,9 @@ def attention_train_fp8(q, k, v, kf: int, mode: int, softmax_scale: float = 0.0,
     log-sum-exp.  Returns (out bf16, lse fp32 (B, T*H*W, heads), codes
     (q8, k8, v8), scales fp32 (3, 2))."""
     import torch
-    if q.dim() != 6 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one (B, T, H, W, heads, d) shape")
+    if q.dim() != 6:
+        raise ValueError("q must be (B, T, H, W, heads, d)")
+    _check_like(("k", "v"), (k, v), q.shape, q.dtype, q.device)
     B, T, H, W, nh, d = q.shape
     if plan is None:
         plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
@@ -517,7 +557,19 @@ def attention_bwd_fp8(codes, scales, o, dout, lse, kf: int, mode: int, softmax_s
     attention_train_fp8) and of dO.  Returns (dq, dk, dv) bf16."""
     import torch
     q8, k8, v8 = codes
+    if q8.dim() != 6:
+        raise ValueError("the codes must be (B, T, H, W, heads, d)")
+    _check_like(("q8", "k8", "v8"), (q8, k8, v8), q8.shape, torch.uint8, q8.device)
+    for t in (q8, k8, v8):
+        if not t.is_contiguous():
+            raise ValueError("the codes must be contiguous")
+    _check_like(("scales",), (scales,), (3, 2), torch.float32, q8.device)
+    if not scales.is_contiguous():
+        raise ValueError("scales must be contiguous")
+    _check_like(("o",), (o,), q8.shape, torch.bfloat16, q8.device)
+    _check_like(("dout",), (dout,), q8.shape, dout.dtype, q8.device)
     B, T, H, W, nh, d = q8.shape
+    _check_lse(lse, B, T * H * W, nh, q8.device)
     if plan is None:
         plan = skiparse_plan_init(B, T, H, W, nh, d, kf, mode)
     dscale = torch.empty(2, dtype=torch.float32, device=o.device)

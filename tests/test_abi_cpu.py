@@ -404,3 +404,49 @@ def test_wrappers_reject_mismatched_outputs():
         blk(x, out=torch.empty((1, 2, 4, 6, 128), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="out must be"):
         sk.quantize_fp8(q, scale_out=torch.empty(3, dtype=torch.float32))
+
+
+def test_wrappers_reject_mismatched_inputs():
+    """Inputs a kernel reads at a fixed element size are checked on the host:
+    mixed dtypes, a missing or misshapen e4m3 descale, a log-sum-exp of the
+    wrong shape or dtype, and quantizer inputs other than bf16 or fp32 (each
+    would otherwise be read past its end or at the wrong size)."""
+    import torch
+    shp = (1, 2, 4, 6, 2, 64)
+    N = 2 * 4 * 6
+    bf = torch.zeros(shp, dtype=torch.bfloat16)
+    f32 = torch.zeros(shp, dtype=torch.float32)
+    u8 = torch.zeros(shp, dtype=torch.uint8)
+    lse = torch.zeros((1, N, 2), dtype=torch.float32)
+    with pytest.raises(TypeError, match="k must be"):
+        sk.attention(f32, bf, bf, 2, sk.MODE_TOKEN)
+    with pytest.raises(ValueError, match="descale_qkv"):
+        sk.attention(u8, u8, u8, 2, sk.MODE_TOKEN)
+    with pytest.raises(ValueError, match="descale_qkv must have shape"):
+        sk.attention(u8, u8, u8, 2, sk.MODE_TOKEN, descale_qkv=torch.ones(6))
+    with pytest.raises(TypeError, match="q must be"):
+        sk.attention_train(f32, f32, f32, 2, sk.MODE_TOKEN)
+    with pytest.raises(ValueError, match="v must have shape"):
+        sk.attention_train(bf, bf, bf[..., :32], 2, sk.MODE_TOKEN)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        sk.attention_bwd(bf, bf, bf, bf, bf, lse[:, :-1], 2, sk.MODE_TOKEN)
+    with pytest.raises(TypeError, match="lse must be"):
+        sk.attention_bwd(bf, bf, bf, bf, bf, lse.double(), 2, sk.MODE_TOKEN)
+    with pytest.raises(TypeError, match="dout must be"):
+        sk.attention_bwd(bf, bf, bf, bf, f32, lse, 2, sk.MODE_TOKEN)
+    with pytest.raises(ValueError, match="lse must be contiguous"):
+        sk.attention_bwd(bf, bf, bf, bf, bf, torch.zeros((1, 2, N), dtype=torch.float32).transpose(1, 2), 2,
+                         sk.MODE_TOKEN)
+    scales = torch.ones((3, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="v8 must have shape"):
+        sk.attention_bwd_fp8((u8, u8, u8[..., :32]), scales, bf, bf, lse, 2, sk.MODE_TOKEN)
+    with pytest.raises(TypeError, match="o must be"):
+        sk.attention_bwd_fp8((u8, u8, u8), scales, f32, bf, lse, 2, sk.MODE_TOKEN)
+    with pytest.raises(ValueError, match="scales must have shape"):
+        sk.attention_bwd_fp8((u8, u8, u8), scales[:2], bf, bf, lse, 2, sk.MODE_TOKEN)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        sk.attention_bwd_fp8((u8, u8, u8), scales, bf, bf, lse[..., :1], 2, sk.MODE_TOKEN)
+    with pytest.raises(TypeError, match="k must be"):
+        sk.attention_train_fp8(bf, f32, bf, 2, sk.MODE_TOKEN)
+    with pytest.raises(TypeError, match="bfloat16 or float32"):
+        sk.quantize_fp8(torch.zeros(shp, dtype=torch.float16))
