@@ -191,6 +191,18 @@ def test_bwd_workload_sampled(mode):
     check_full_size(w.shape, w.k, mode, w.seed + 10, heads_q=[0, w.heads - 1], heads_kv=[w.heads // 2])
 
 
+def test_bwd_k1_workload_sampled():
+    """Full attention (k = 1) at the 720P-5s shape: one subsequence of 75600
+    tokens, so the training forward and the dQ kernel stream 1182 and 2363 key
+    tiles per work-group, the running max and sums run over the whole frame
+    stack, and dQ takes rows from the index function (n is past the token
+    table).  Sampled dQ rows in two heads against the oracle.  dK and dV run
+    the same kernel as at k = 2 with a longer query loop; the oracle's rows for
+    them would take minutes here (every query's softmax over 75600 keys)."""
+    w = wl.WORKLOADS["720p_5s"]
+    check_full_size(w.shape, 1, 0, w.seed + 30, heads_q=[0, w.heads - 1], heads_kv=[], per_sub=24)
+
+
 def test_bwd_index_function_path():
     """n = 24200 members exceeds the token-table capacity: rows come from the
     index function."""
